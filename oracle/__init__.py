@@ -1,0 +1,294 @@
+"""Plain CPU oracle for one rank's share of a ZeRO-3 data-parallel step.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the benchmark's ``cpu_baseline`` leg may import, call or execute anything in
+this package.  It shares no code with the GPU library and imports nothing from
+it; the two meet only at the seeded input generators of ``zr_workloads``.
+
+What is here, each part written from the ZeRO-3 web pages:
+
+* ``Layout``: the flat, padded, rank-contiguous partition with small-tensor
+  persistence (pure Python integers, no vectorisation).
+* ``ledger_closed_form`` / ``Layout.ledger_bytes``: per-rank model-state bytes.
+* ``pack`` / ``unpack``: bit copies between per-tensor bf16 views and the flat
+  buffer (numpy slice copies, one fragment at a time).
+* ``reduce`` / ``adamw`` / bf16 conversion: scalar C loops in ``zr_oracle.c``
+  (built by ``oracle/build.py`` with gcc, no fast-math, no FP contraction).
+
+Parity pins for every function live in ``tests/test_oracle_*.py``; all of them
+are pinned (none is "parity unpinned").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from fractions import Fraction
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import build as _build
+
+DEFAULT_PERSIST_THRESHOLD = 100_000
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIBRARY):
+            _build.build()
+        lib = ctypes.CDLL(_build.LIBRARY)
+        i64, i32 = ctypes.c_int64, ctypes.c_int32
+        p = ctypes.c_void_p
+        d = ctypes.c_double
+        lib.zr_oracle_bf16_from_f32.argtypes = [p, i64, p]
+        lib.zr_oracle_bf16_from_f32.restype = None
+        lib.zr_oracle_f32_from_bf16.argtypes = [p, i64, p]
+        lib.zr_oracle_f32_from_bf16.restype = None
+        lib.zr_oracle_reduce.argtypes = [p, i32, i64, p]
+        lib.zr_oracle_reduce.restype = None
+        lib.zr_oracle_adamw.argtypes = [p, p, p, p, p, i64, d, d, d, d, d, d, i64]
+        lib.zr_oracle_adamw.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _check(a: np.ndarray, dtype, name: str):
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or not a.flags["C_CONTIGUOUS"]:
+        raise TypeError(f"{name} must be a C-contiguous numpy array of {np.dtype(dtype).name}")
+
+
+# ------------------------------------------------------------------ bf16 ----
+
+def bf16_from_f32(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+
+    The concept page's Stage 1 mechanism converts the updated fp32 master to the
+    16-bit working copy; the ledger section of the ddp-to-zero blog makes that
+    copy bf16.  Round-to-nearest-even is the reading taken for the conversion.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().zr_oracle_bf16_from_f32(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def f32_from_bf16(h: np.ndarray) -> np.ndarray:
+    """bf16 bits -> fp32 (exact widening)."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    _load().zr_oracle_f32_from_bf16(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+# ---------------------------------------------------------------- reduce ----
+
+def reduce(contribs: Sequence[np.ndarray], out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Mean of n bf16 gradient contributions, element by element (bf16 bits in,
+    bf16 bits out), accumulated in fp32 in ascending contribution order.
+
+    Follows the ddp-to-zero blog, "ZeRO-2: why gradients can be sharded" (the
+    averaged-gradient ReduceScatter worked example).  ``out`` may be
+    ``contribs[0]`` itself.
+    """
+    if len(contribs) < 1:
+        raise ValueError("need at least one contribution")
+    numel = contribs[0].size
+    for k, c in enumerate(contribs):
+        _check(c, np.uint16, f"contribs[{k}]")
+        if c.size != numel:
+            raise ValueError("contributions differ in length")
+    if out is None:
+        out = np.empty(numel, dtype=np.uint16)
+    _check(out, np.uint16, "out")
+    if out.size != numel:
+        raise ValueError("out has the wrong length")
+    table = (ctypes.c_void_p * len(contribs))(*[_ptr(c) for c in contribs])
+    _load().zr_oracle_reduce(ctypes.cast(table, ctypes.c_void_p), len(contribs), numel, _ptr(out))
+    return out
+
+
+# ----------------------------------------------------------------- AdamW ----
+
+def adamw(grad: np.ndarray, master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
+          param_out: Optional[np.ndarray], *, lr: float, beta1: float, beta2: float, eps: float,
+          weight_decay: float, step: int, grad_scale: float = 1.0) -> None:
+    """One AdamW step in place on fp32 master / exp_avg / exp_avg_sq from a bf16
+    gradient, then the bf16 copy of the new master into ``param_out`` (if given).
+
+    Computed in double, stored in the pages' dtypes (fp32 states, bf16 copy).
+    Follows the ddp-to-zero blog's ledger section and "ZeRO-1: why optimizer
+    states can be sharded", the concept page's Stage 1 mechanism, and the
+    tutorial's section 3.1 AdamW configuration; the formula is the published
+    decoupled-weight-decay Adam (see zr_oracle.c).
+    """
+    n = grad.size
+    _check(grad, np.uint16, "grad")
+    for name, a in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _check(a, np.float32, name)
+        if a.size != n:
+            raise ValueError(f"{name} has the wrong length")
+    pp = None
+    if param_out is not None:
+        _check(param_out, np.uint16, "param_out")
+        if param_out.size != n:
+            raise ValueError("param_out has the wrong length")
+        pp = _ptr(param_out)
+    if step < 1:
+        raise ValueError("step must be >= 1")
+    _load().zr_oracle_adamw(_ptr(grad), _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), pp, n,
+                            float(lr), float(beta1), float(beta2), float(eps),
+                            float(weight_decay), float(grad_scale), int(step))
+
+
+# ---------------------------------------------------------------- layout ----
+
+class Layout:
+    """Flat, padded partition of a tensor list over ``n_d`` data-parallel ranks.
+
+    Rules, each from the pages:
+
+    * A tensor with fewer than ``threshold`` elements is persistent: it is not
+      partitioned and stays whole on every rank (Zero-3 parameter-partitioning
+      article (hotelren.com): the quick-start config's
+      stage3_param_persistence_threshold of 100000, and the small-parameter
+      residency paragraph; "below" is read as strictly less than).
+    * The other tensors are concatenated in list order into one flat buffer
+      with no gaps between tensors (tutorial section 3.2, contiguous_gradients).
+    * The flat buffer is split into ``n_d`` equal contiguous slices in rank
+      order: rank 0 owns the first slice, rank 1 the next (tutorial section 2.1;
+      the ddp-to-zero blog's 8-parameter example in "ZeRO-3: why parameters can
+      be sharded", where rank r holds elements 2r and 2r+1).
+    * The pages assume n_d divides the element count; where it does not, the
+      buffer is padded with zeros at its end up to the next multiple of n_d.
+    * Persistent tensors are laid out one after another, in list order, in a
+      separate replicated region.
+    """
+
+    def __init__(self, numels: Sequence[int], n_d: int, threshold: int = DEFAULT_PERSIST_THRESHOLD):
+        numels = [int(x) for x in numels]
+        if n_d < 1:
+            raise ValueError("n_d must be >= 1")
+        if threshold < 0:
+            raise ValueError("threshold must be >= 0")
+        if any(x < 0 for x in numels):
+            raise ValueError("negative numel")
+        self.numels = numels
+        self.n_d = int(n_d)
+        self.threshold = int(threshold)
+        self.persistent = [x < self.threshold for x in numels]
+        self.offset: List[int] = []
+        flat = 0
+        persist = 0
+        for x, is_persistent in zip(numels, self.persistent):
+            if is_persistent:
+                self.offset.append(persist)
+                persist += x
+            else:
+                self.offset.append(flat)
+                flat += x
+        self.psi = sum(numels)
+        self.psi_part = flat
+        self.psi_persist = persist
+        # smallest multiple of n_d that is >= psi_part
+        self.psi_pad = -(-self.psi_part // self.n_d) * self.n_d
+        self.shard = self.psi_pad // self.n_d
+        self.n_partitioned = sum(1 for q in self.persistent if not q)
+        self.n_persistent = len(numels) - self.n_partitioned
+
+    def rank_range(self, rank: int) -> Tuple[int, int]:
+        """Flat elements [begin, end) owned by ``rank``."""
+        if not 0 <= rank < self.n_d:
+            raise IndexError("rank out of range")
+        return rank * self.shard, (rank + 1) * self.shard
+
+    def owner(self, j: int) -> int:
+        """Rank owning flat element j (0 <= j < psi_pad)."""
+        return j // self.shard
+
+    def fragments(self, begin: int, end: int) -> List[Tuple[int, int, int, int]]:
+        """Pieces of partitioned tensors inside flat [begin, end), in flat order,
+        as (tensor, offset inside the tensor, flat offset, element count)."""
+        if not 0 <= begin <= end <= self.psi_pad:
+            raise ValueError("range outside [0, psi_pad]")
+        out = []
+        for t, x in enumerate(self.numels):
+            if self.persistent[t] or x == 0:
+                continue
+            lo = max(begin, self.offset[t])
+            hi = min(end, self.offset[t] + x)
+            if lo < hi:
+                out.append((t, lo - self.offset[t], lo, hi - lo))
+        return out
+
+    def ledger_bytes(self, stage: int) -> int:
+        """Exact per-rank model-state bytes for this layout (16 B per element as
+        2 bf16 param + 2 bf16 grad + 12 fp32 master/m/v).  Persistent tensors
+        keep all of their state on every rank; partitioned state is one shard
+        of ``shard`` elements (padding included)."""
+        owned = self.shard + self.psi_persist
+        if stage == 0:
+            return 16 * self.psi
+        if stage == 1:
+            return 2 * self.psi + 2 * self.psi + 12 * owned
+        if stage == 2:
+            return 2 * self.psi + 14 * owned
+        if stage == 3:
+            return 16 * owned
+        raise ValueError("stage must be 0..3")
+
+
+def ledger_closed_form(psi: int, n_d: int, stage: int) -> Fraction:
+    """Per-rank model-state bytes from the pages' closed forms (mixed precision
+    with Adam: 16 bytes per parameter).
+
+    Stage 0 (plain data parallel) 16 psi; stage 1 4 psi + 12 psi / n_d;
+    stage 2 2 psi + 14 psi / n_d; stage 3 16 psi / n_d = (2+2+12) psi / n_d.
+    Follows the concept page's per-stage memory formulas and their summary
+    table, and the encyclopedia entry's principle section ((2+2+K) psi / N_d
+    with K = 12 for Adam).
+    """
+    psi = Fraction(psi)
+    if stage == 0:
+        return 16 * psi
+    if stage == 1:
+        return 4 * psi + 12 * psi / n_d
+    if stage == 2:
+        return 2 * psi + 14 * psi / n_d
+    if stage == 3:
+        return (2 + 2 + 12) * psi / n_d
+    raise ValueError("stage must be 0..3")
+
+
+# ----------------------------------------------------------- pack/unpack ----
+
+View = Optional[Tuple[np.ndarray, int]]  # (bf16 bits of elements [first, first+len), first)
+
+
+def pack(layout: Layout, views: Sequence[View], begin: int, end: int) -> np.ndarray:
+    """Flat bf16 elements [begin, end) gathered from per-tensor views; padding
+    and anything outside the tensors is zero.  Bit copy.
+
+    This is the local side of the AllGather / contiguous buffer: the ddp-to-zero
+    blog's ZeRO-1 example reassembles [9] and [18] into [9, 18]; the tutorial's
+    section 3.2 keeps gradients in one contiguous buffer.
+    """
+    flat = np.zeros(end - begin, dtype=np.uint16)
+    for t, toff, foff, n in layout.fragments(begin, end):
+        arr, first = views[t]
+        flat[foff - begin: foff - begin + n] = arr[toff - first: toff - first + n]
+    return flat
+
+
+def unpack(layout: Layout, flat: np.ndarray, begin: int, end: int, views: Sequence[View]) -> None:
+    """Scatter flat bf16 elements [begin, end) back into the per-tensor views
+    (in place); the padding is not written anywhere.  Bit copy."""
+    for t, toff, foff, n in layout.fragments(begin, end):
+        arr, first = views[t]
+        arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n]

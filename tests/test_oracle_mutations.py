@@ -1,0 +1,55 @@
+"""Pin strength: plant one plausible mistake at a time in a scratch copy of the
+oracle (CPU only) and check that the oracle's pin tests then fail."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+C = "oracle/zr_oracle.c"
+PY = "oracle/__init__.py"
+MUTATIONS = [
+    ("dropped weight decay", C, "th = th * decay;", "th = th;"),
+    ("wrong update sign", C, "th = th - lr * m_hat", "th = th + lr * m_hat"),
+    ("eps inside the root", C, "(sqrt(v_hat) + eps)", "sqrt(v_hat + eps)"),
+    ("no first-moment bias correction", C, "double m_hat = m / bias1;", "double m_hat = m;"),
+    ("wrong second-moment correction", C, "double v_hat = v / bias2;", "double v_hat = v / bias1;"),
+    ("g instead of g^2", C, "(1.0 - beta2) * g * g", "(1.0 - beta2) * g"),
+    ("beta1 for 1 - beta1", C, "m = beta1 * m + (1.0 - beta1) * g;", "m = beta1 * m + beta1 * g;"),
+    ("grad_scale ignored", C, "double g = (double)bf16_to_f32(grad[i]) * grad_scale;",
+     "double g = (double)bf16_to_f32(grad[i]);"),
+    ("mean over n + 1", C, "float mean = sum / (float)n;", "float mean = sum / (float)(n + 1);"),
+    ("last contribution dropped", C, "for (int32_t k = 1; k < n; ++k)", "for (int32_t k = 1; k < n - 1; ++k)"),
+    ("ties always up", C, "(lower == 0x8000u && (upper & 1u))", "(lower == 0x8000u)"),
+    ("bf16 copy off by one bit", C, "param_out[i] = f32_to_bf16(master[i]);",
+     "param_out[i] = (uint16_t)(f32_to_bf16(master[i]) ^ 1);"),
+    ("threshold inclusive", PY, "self.persistent = [x < self.threshold", "self.persistent = [x <= self.threshold"),
+    ("padding always added", PY, "self.psi_pad = -(-self.psi_part // self.n_d) * self.n_d",
+     "self.psi_pad = (self.psi_part // self.n_d) * self.n_d + self.n_d"),
+    ("stage-2 ledger uses 12", PY, "return 2 * self.psi + 14 * owned", "return 2 * self.psi + 12 * owned"),
+    ("stage-1 closed form uses 14", PY, "return 4 * psi + 12 * psi / n_d", "return 4 * psi + 14 * psi / n_d"),
+    ("fragment one too long", PY, "out.append((t, lo - self.offset[t], lo, hi - lo))",
+     "out.append((t, lo - self.offset[t], lo, hi - lo + (1 if hi < end else 0)))"),
+    ("unpack reversed", PY, "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n]",
+     "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n][::-1]"),
+]
+
+PIN_TESTS = ["tests/test_oracle_numerics.py", "tests/test_oracle_layout.py", "tests/test_oracle_ledger.py"]
+
+
+@pytest.mark.parametrize("what,path,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path, what, path, old, new):
+    for d in ("oracle", "tests", "zr_workloads"):
+        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+                        ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    target = tmp_path / path
+    text = target.read_text()
+    assert text.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    target.write_text(text.replace(old, new))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_TESTS],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"planted mistake '{what}' passed every pin:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout
