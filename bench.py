@@ -1,0 +1,260 @@
+"""Benchmark: one rank's share of a ZeRO-3 step on one MI355X.
+
+A step is one pass of the whole hot path over the rank's shard:
+  1. zr_pack         this rank's own bf16 gradient (per-tensor views) -> flat
+                     contribution 0 of its slice
+  2. zr_reduce_slice mean of the n bf16 contributions -> bf16 gradient shard
+  3. zr_adamw_step   fused AdamW on fp32 master / m / v, bf16 copy written into
+                     the rank's slot of the flat parameter buffer
+  4. zr_unpack       that slot -> per-tensor bf16 parameter views
+(the layout, a host object, is built once).  Inputs are synthetic, seeded and
+already resident in HBM when the timed region starts.
+
+Prints ONE JSON line.  `value` is shard elements per second of the whole step;
+`roofline` is the fused AdamW kernel's algorithmic HBM bandwidth (28 bytes per
+element) from HIP events around each of its launches, against the 8 TB/s
+MI355X peak; `cpu_baseline` is the oracle, as it stands, timed on the host
+cores over a bounded prefix of the same shard.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD specification
+METRIC = "shard AdamW step elements/s + achieved HBM GB/s vs peak (7B, N_d=4 shard)"
+COUNTERS = os.path.join(ROOT, "profiles", "adamw_flat7e9_counters.json")
+KERNEL_SOURCES = ["zero_sharded_optimizer_zr_amd/csrc/adamw.hip", "zero_sharded_optimizer_zr_amd/csrc/zr_device.hpp"]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--workload", default="flat_7e9_nd4_r0")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample", type=int, default=1 << 28, help="shard prefix the oracle runs over")
+    p.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle step until this much time")
+    p.add_argument("--copy-calibration", type=int, default=0,
+                   help="also run N plain copies of 4 GiB (reference kernel for HBM counters)")
+    return p.parse_args()
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(per_launch_bytes):
+    """HBM bytes per AdamW launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    counts (scaled by the copy-kernel calibration), if they were taken on the
+    current kernel source; else None."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        c = json.load(f)
+    if c.get("kernel_hash") != kernel_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs one GPU only (asked for --gpus {args.gpus}): this build shards nothing across GPUs",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import zero_sharded_optimizer_zr_amd as zr
+    from zr_workloads import BY_NAME, synth
+
+    w = BY_NAME[args.workload]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    hp = w.hparams
+    t_step = w.steps[0]
+
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    info = zr.zr_layout_query(lay)
+    b, e = zr.zr_layout_rank_range(lay, w.rank)
+    S = e - b
+    frags = zr.zr_layout_fragments(lay, b, e)
+    n = w.n_contrib
+    print(f"[bench] {w.name}: shard [{b}, {e}) = {S} elements, {len(frags)} fragments, {n} contributions",
+          file=sys.stderr, flush=True)
+
+    # this rank's gradient and parameters as per-tensor windows covering the shard
+    def windows(seed):
+        out = [None] * len(w.numels)
+        for t, toff, _, cnt in frags:
+            out[t] = (synth.normal_bf16(cnt, w.grad_std, seed + t, dev), toff)
+        return out
+
+    own_grad = windows(7000)
+    params = [None if v is None else (torch.empty_like(v[0]), v[1]) for v in own_grad]
+    contribs = [torch.empty(S, dtype=torch.bfloat16, device=dev)]
+    contribs += synth.contributions(w, S, device=dev)[1:]
+    grad = torch.empty(S, dtype=torch.bfloat16, device=dev)
+    st = synth.shard_state(w, S, device=dev)
+    master, m, v = st["master"], st["exp_avg"], st["exp_avg_sq"]
+    flat_param = torch.empty(S, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    print(f"[bench] inputs resident: {torch.cuda.memory_allocated() / 1e9:.1f} GB", file=sys.stderr, flush=True)
+
+    names = ("pack", "reduce", "adamw", "unpack")
+    events = {k: [] for k in names}
+
+    def step(record):
+        def ev():
+            x = torch.cuda.Event(enable_timing=True)
+            x.record(stream)
+            return x
+        t0 = ev() if record else None
+        zr.zr_pack(lay, own_grad, contribs[0], b, e, stream=stream)
+        t1 = ev() if record else None
+        zr.zr_reduce_slice(contribs, grad, stream=stream)
+        t2 = ev() if record else None
+        zr.zr_adamw_step(grad, master, m, v, flat_param, step=t_step, stream=stream, **hp)
+        t3 = ev() if record else None
+        zr.zr_unpack(lay, flat_param, b, e, params, stream=stream)
+        if record:
+            t4 = ev()
+            for k, (x, y) in zip(names, ((t0, t1), (t1, t2), (t2, t3), (t3, t4))):
+                events[k].append((x, y))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - start
+    print(f"[bench] {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
+
+    for _ in range(args.copy_calibration):
+        a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
+        c = torch.empty_like(a)
+        c.copy_(a)
+        torch.cuda.synchronize()
+        del a, c
+
+    bytes_per = {"pack": 4 * S, "reduce": (2 * n + 2) * S, "adamw": 28 * S, "unpack": 4 * S}
+    kernels = {}
+    for k in names:
+        ms = [x.elapsed_time(y) for x, y in events[k]]
+        avg = float(np.mean(ms))
+        kernels[k] = {"ms_avg": round(avg, 4), "ms_min": round(float(np.min(ms)), 4),
+                      "algorithmic_bytes": bytes_per[k],
+                      "GBps": round(bytes_per[k] / (avg * 1e-3) / 1e9, 1)}
+    ms_per_step = elapsed / args.steps * 1e3
+    step_bytes = sum(bytes_per.values())
+    adamw_ms = kernels["adamw"]["ms_avg"]
+    achieved = bytes_per["adamw"] / (adamw_ms * 1e-3) / 1e9
+    traffic = measured_traffic(bytes_per["adamw"])
+
+    result = {
+        "metric": METRIC,
+        "value": S / (ms_per_step * 1e-3),
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "psi": info["psi"], "n_d": w.n_d, "rank": w.rank, "shard": S,
+                   "contributions": n, "adamw_step": t_step, "path": "pack+reduce+adamw+unpack",
+                   "step_algorithmic_bytes": step_bytes,
+                   "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "kernel": "zr_adamw_step", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": bytes_per["adamw"],
+                     "bytes_per_element": 28},
+        "kernels": kernels,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, lay, frags, b, min(args.cpu_sample, S), own_grad, contribs,
+                                              st, hp, t_step, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, lay, frags, b, sample, own_grad, contribs, st, hp, t_step, min_seconds):
+    """The oracle, unchanged, over the shard prefix [b, b + sample): the same four
+    steps, split into contiguous sub-ranges run on all host cores (the oracle's C
+    loops release the GIL), repeated as consecutive steps until `min_seconds`
+    have passed.  Inputs are copied to host before the clock starts."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    cores = len(os.sched_getaffinity(0))
+    bits = lambda t: t.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref = oracle.Layout(w.numels, w.n_d, w.threshold)
+    e = b + sample
+    views = [None] * len(w.numels)
+    for t, toff, foff, cnt in frags:
+        lo, hi = max(foff, b), min(foff + cnt, e)
+        if lo < hi:
+            tlo = toff + (lo - foff)
+            views[t] = (bits(own_grad[t][0][tlo - own_grad[t][1]: tlo - own_grad[t][1] + (hi - lo)]).copy(), tlo)
+    peers = [bits(c[:sample]).copy() for c in contribs[1:]]
+    master = st["master"][:sample].cpu().numpy().copy()
+    m = st["exp_avg"][:sample].cpu().numpy().copy()
+    v = st["exp_avg_sq"][:sample].cpu().numpy().copy()
+    out_views = [None if x is None else (np.empty_like(x[0]), x[1]) for x in views]
+    contrib0 = np.empty(sample, np.uint16)
+    grad = np.empty(sample, np.uint16)
+    param = np.empty(sample, np.uint16)
+    cuts = np.linspace(0, sample, cores + 1).astype(np.int64)
+
+    def part(i):
+        lo, hi = int(cuts[i]), int(cuts[i + 1])
+        contrib0[lo:hi] = oracle.pack(ref, views, b + lo, b + hi)
+        oracle.reduce([contrib0[lo:hi]] + [p[lo:hi] for p in peers], out=grad[lo:hi])
+        oracle.adamw(grad[lo:hi], master[lo:hi], m[lo:hi], v[lo:hi], param[lo:hi], step=t_step, **hp)
+        oracle.unpack(ref, param[lo:hi], b + lo, b + hi, out_views)
+
+    reps = 0
+    with ThreadPoolExecutor(cores) as pool:
+        t0 = time.perf_counter()
+        while True:
+            list(pool.map(part, range(cores)))
+            reps += 1
+            secs = time.perf_counter() - t0
+            if secs >= min_seconds:
+                break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    return {"value": sample * reps / secs, "unit": "elements/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {sample} elements of the same shard, whole step (pack, reduce, AdamW, unpack) "
+                      f"repeated {reps} times: {secs:.2f} s on {cores} threads of {cpu}"}
+
+
+if __name__ == "__main__":
+    main()

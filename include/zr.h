@@ -1,0 +1,257 @@
+/*
+ * zr.h -- C ABI of libzr: one data-parallel rank's share of a ZeRO-3 training
+ * step on one AMD Instinct MI355X (gfx950).
+ *
+ * The share has four parts, each an entry point below:
+ *   1. a flat, padded partition layout with rank slices and small-tensor
+ *      persistence                                  (zr_layout_*)
+ *   2. the local arithmetic of the gradient ReduceScatter: the mean of n bf16
+ *      gradient contributions over the owned slice  (zr_reduce_slice)
+ *   3. a fused mixed-precision AdamW step on the slice (zr_adamw_step)
+ *   4. bit copies between per-tensor bf16 views and the flat buffer
+ *                                                    (zr_pack / zr_unpack)
+ *
+ * Sources are web pages on DeepSpeed ZeRO-3, cited by title and section:
+ *   [ENC]  "DeepSpeed ZeRO-3", encyclopedia entry (baike.kuaisou.com)
+ *   [BLOG] "From DDP to ZeRO: memory sharding", blog (111qqz.com)
+ *   [TUT]  ZeRO-1/2/3 tutorial (cnhsyj.com), numbered sections
+ *   [ART]  "DeepSpeed Zero-3 parameter partitioning and on-demand access",
+ *          article (hotelren.com)
+ *   [CON]  "ZeRO-1/2/3 (Zero Redundancy Optimizer, three stages)",
+ *          concept page (compassingai.com)
+ *
+ * Conventions for every call:
+ *   - Validation first.  Every argument is checked on the host before any HIP
+ *     call; a rejected call launches nothing and writes nothing, returns a
+ *     non-zero zr_status and sets the calling thread's zr_last_error().
+ *   - Asynchronous.  Device work is enqueued on `stream` (a hipStream_t; NULL is
+ *     the null stream) and the call returns without synchronising.  A failed
+ *     launch returns ZR_EHIP with the HIP error string in zr_last_error().
+ *   - The library never allocates device memory.  Every device buffer belongs to
+ *     the caller and must stay alive until the enqueued work has finished.
+ *   - Element counts and offsets are int64.  bf16 buffers need 2-byte and fp32
+ *     buffers 4-byte alignment (else ZR_EALIGN); 16-byte alignment is not
+ *     required and gives the same bits as aligned buffers.
+ *   - bf16 data is passed as raw 16-bit patterns (void*).
+ */
+#ifndef ZR_H
+#define ZR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported from libzr.so (the library is built with hidden visibility). */
+#define ZR_API __attribute__((visibility("default")))
+
+#define ZR_ABI_VERSION 1
+
+typedef int32_t zr_status;
+#define ZR_OK      0
+#define ZR_EINVAL  1   /* malformed argument: NULL pointer, negative count, bad hyper-parameter, overlap */
+#define ZR_ERANGE  2   /* index, rank or range outside what the layout or buffer allows; capacity too small */
+#define ZR_EALIGN  3   /* buffer not naturally aligned for its element type */
+#define ZR_ENOMEM  4   /* host allocation failed */
+#define ZR_EHIP    5   /* HIP launch error */
+
+/* Opaque, immutable after creation; safe to read from many threads at once. */
+typedef struct zr_layout zr_layout;
+
+typedef struct zr_layout_info {
+    int64_t psi;            /* elements in all tensors */
+    int64_t psi_part;       /* elements in partitioned tensors */
+    int64_t psi_persist;    /* elements in persistent (replicated) tensors */
+    int64_t psi_pad;        /* flat buffer length: psi_part rounded up to a multiple of n_d */
+    int64_t shard;          /* elements per rank: psi_pad / n_d */
+    int64_t threshold;      /* persistence threshold the layout was built with */
+    int32_t n_d;            /* data-parallel ranks */
+    int32_t n_tensors;
+    int32_t n_partitioned;
+    int32_t n_persistent;
+} zr_layout_info;
+
+/* A piece of one partitioned tensor inside a flat range. */
+typedef struct zr_fragment {
+    int32_t tensor;         /* index in the list given to zr_layout_create */
+    int32_t reserved;       /* 0 */
+    int64_t tensor_offset;  /* first element of the piece inside the tensor */
+    int64_t flat_offset;    /* first element of the piece inside the flat buffer */
+    int64_t numel;          /* elements in the piece (> 0) */
+} zr_fragment;
+
+/* A device bf16 window holding elements [first, first + count) of one tensor. */
+typedef struct zr_view {
+    void   *ptr;
+    int64_t first;
+    int64_t count;
+} zr_view;
+
+/* AdamW hyper-parameters.  The library derives the per-step scalars in double
+ * and rounds each once to fp32 for the device. */
+typedef struct zr_adamw_hparams {
+    double  lr;
+    double  beta1;
+    double  beta2;
+    double  eps;
+    double  weight_decay;
+    double  grad_scale;     /* the bf16 gradient is multiplied by this first (1.0 for a mean) */
+    int64_t step;           /* t >= 1, the step's bias-correction exponent */
+} zr_adamw_hparams;
+
+/* ------------------------------------------------------------- layout ---- */
+
+/*
+ * Build the partition of a tensor list over n_d ranks.
+ *
+ * [ART] minimal ZeRO-3 config and its small-parameter residency paragraph:
+ * tensors with fewer than `persist_threshold` elements (default 100000) are not
+ * partitioned; they stay whole on every rank, in a separate replicated region
+ * laid out in list order.  [TUT] 3.2 (contiguous gradient buffer) and 2.1 (rank
+ * 0 owns the first 1/N_d, rank 1 the next): the other tensors are concatenated
+ * in list order, with no gaps, into one flat buffer that is cut into n_d equal
+ * contiguous slices; [BLOG] "ZeRO-3: why parameters can be sharded too" (8
+ * parameters on 4 GPUs).  The pages assume n_d divides the count; here the flat
+ * buffer is padded at its end to psi_pad = ceil(psi_part / n_d) * n_d, and the
+ * padding is zero.
+ *
+ * numels: host array of n_tensors element counts (>= 0; 0 is allowed).
+ * n_tensors >= 0; n_d >= 1; persist_threshold >= 0 (0: nothing is persistent).
+ * On success *out owns host memory released by zr_layout_destroy.
+ * Errors: ZR_EINVAL (NULL pointer, negative count, n_d < 1, negative threshold,
+ * int64 overflow of a sum), ZR_ENOMEM.
+ */
+ZR_API zr_status zr_layout_create(const int64_t *numels, int32_t n_tensors, int32_t n_d,
+                           int64_t persist_threshold, zr_layout **out);
+
+/* Free a layout; NULL is ignored. */
+ZR_API void zr_layout_destroy(zr_layout *layout);
+
+/* Sizes and counts of a layout.  Errors: ZR_EINVAL (NULL). */
+ZR_API zr_status zr_layout_query(const zr_layout *layout, zr_layout_info *out);
+
+/* Tensor t: *persistent = 1 if replicated, and *offset = its offset in the
+ * persistent region; else *persistent = 0 and *offset = its flat offset.
+ * Either output pointer may be NULL.  Errors: ZR_EINVAL, ZR_ERANGE (t). */
+ZR_API zr_status zr_layout_tensor(const zr_layout *layout, int32_t t, int32_t *persistent, int64_t *offset);
+
+/* Flat range [begin, end) = [rank * shard, (rank + 1) * shard) owned by rank
+ * ([TUT] 2.1).  Errors: ZR_EINVAL, ZR_ERANGE (rank outside [0, n_d)). */
+ZR_API zr_status zr_layout_rank_range(const zr_layout *layout, int32_t rank, int64_t *begin, int64_t *end);
+
+/*
+ * The pieces of partitioned tensors inside flat [begin, end), 0 <= begin <=
+ * end <= psi_pad, in flat order ([BLOG] "ZeRO-3: why parameters can be sharded
+ * too": one tensor may be split across ranks).  Empty tensors yield no piece.
+ * Two-call idiom: writes min(count, cap) entries to out (out may be NULL when
+ * cap is 0) and sets *n to the full count; returns ZR_ERANGE if cap < count.
+ * Errors: ZR_EINVAL, ZR_ERANGE (range, capacity).
+ */
+ZR_API zr_status zr_layout_fragments(const zr_layout *layout, int64_t begin, int64_t end,
+                              zr_fragment *out, int32_t cap, int32_t *n);
+
+/*
+ * Exact per-rank model-state bytes of this layout at ZeRO stage 0..3, 16 bytes
+ * per element as 2 (bf16 param) + 2 (bf16 grad) + 12 (fp32 master, m, v):
+ * [BLOG] ledger section; [CON] per-stage memory formulas (16 psi;
+ * 4 psi + 12 psi/N_d; 2 psi + 14 psi/N_d; 16 psi/N_d); [ENC] principle section.
+ * Owned state is one shard (padding included) plus every persistent tensor:
+ *   stage 0: 16 psi
+ *   stage 1: 4 psi + 12 (shard + psi_persist)
+ *   stage 2: 2 psi + 14 (shard + psi_persist)
+ *   stage 3: 16 (shard + psi_persist)
+ * Errors: ZR_EINVAL, ZR_ERANGE (stage), ZR_EINVAL on int64 overflow.
+ */
+ZR_API zr_status zr_layout_ledger_bytes(const zr_layout *layout, int32_t stage, int64_t *bytes);
+
+/* -------------------------------------------------------- pack/unpack ---- */
+
+/*
+ * Gather flat elements [begin, end) of the bf16 flat buffer from per-tensor
+ * views: flat[j - begin] = element (j - offset_t) of the tensor t covering j,
+ * and 0 where j lies in the padding.  Every element of the range is written.
+ * This is the local half of the parameter AllGather and of the contiguous
+ * gradient buffer ([BLOG] "ZeRO-1: why optimizer states can be sharded", the
+ * [9] + [18] -> [9, 18] example; [TUT] 3.2 contiguous_gradients).
+ *
+ * views: host array of n_views == n_tensors entries, indexed by tensor.  The
+ * entry of a partitioned tensor with elements in the range must cover those
+ * elements (first <= piece start, piece end <= first + count) else ZR_ERANGE;
+ * other entries (persistent tensors, tensors outside the range) are not read
+ * and may be zeroed.  flat: device pointer to flat element `begin`, holding
+ * end - begin bf16.  The views must not overlap flat.  Bit copy: any 16-bit
+ * pattern (NaN payloads, -0, subnormals) is moved unchanged.
+ * Errors: ZR_EINVAL, ZR_ERANGE, ZR_EALIGN, ZR_EHIP.
+ */
+ZR_API zr_status zr_pack(const zr_layout *layout, const zr_view *views, int32_t n_views,
+                  void *flat, int64_t begin, int64_t end, void *stream);
+
+/*
+ * Inverse of zr_pack: scatter flat elements [begin, end) into the views.  Only
+ * tensor elements inside the range are written; the padding goes nowhere.
+ * Same argument rules as zr_pack.  This is the step after the AllGather that
+ * turns the gathered flat bf16 buffer back into per-tensor parameters
+ * ([BLOG] "ZeRO-1: why optimizer states can be sharded"; [CON] Stage 3
+ * mechanism, gather before compute).
+ */
+ZR_API zr_status zr_unpack(const zr_layout *layout, const void *flat, int64_t begin, int64_t end,
+                    const zr_view *views, int32_t n_views, void *stream);
+
+/* ------------------------------------------------------------- reduce ---- */
+
+/*
+ * out[i] = bf16( (g_0[i] + g_1[i] + ... + g_{n-1}[i]) / n ) for 0 <= i < numel:
+ * the mean of n bf16 gradient contributions, summed in fp32 in ascending k,
+ * divided once by n, rounded to nearest even.  On a rank this is its slice of
+ * the ReduceScatter ([BLOG] "ZeRO-2: why gradients can be sharded too", the
+ * [2,6] + [4,10] -> rank 0 [3], rank 1 [8] example; [CON] Stage 2 and 3
+ * mechanism).  Run over the persistent region it is the AllReduce mean.
+ *
+ * contribs: host array of n device pointers to bf16 [numel], 1 <= n <= 256.
+ * out: device bf16 [numel]; it may be exactly contribs[0] (in place) and must
+ * not otherwise overlap a contribution.  numel >= 0 (0 enqueues nothing).
+ * Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
+ */
+ZR_API zr_status zr_reduce_slice(const void *const *contribs, int32_t n, int64_t numel, void *out, void *stream);
+
+/* -------------------------------------------------------------- AdamW ---- */
+
+/*
+ * One AdamW step on a shard, in place, fused with the bf16 working copy:
+ *   g  = bf16->fp32(grad[i]) * grad_scale
+ *   th = th * (1 - lr * weight_decay)
+ *   m  = beta1 * m + (1 - beta1) * g
+ *   v  = beta2 * v + (1 - beta2) * g * g
+ *   th = th - (lr / (1 - beta1^t)) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ *   param_out[i] = bf16(th)   (round to nearest even)
+ * computed in fp32.  Each element uses only its own gradient and state ([BLOG]
+ * "ZeRO-1: why optimizer states can be sharded"), so N_d shard updates
+ * concatenate to the unsharded update; states are fp32 and the copy is bf16
+ * ([BLOG] ledger section); the copy is made from the updated fp32 master
+ * ([CON] Stage 1 mechanism); AdamW and its hyper-parameters: [TUT] 3.1.  The
+ * formula is decoupled-weight-decay Adam (Loshchilov & Hutter, ICLR 2019).
+ *
+ * grad: device bf16 [numel].  master, exp_avg, exp_avg_sq: device fp32 [numel],
+ * updated in place.  param_out: device bf16 [numel] or NULL (no copy).  No two
+ * of the five buffers may overlap.  numel >= 0.  hp: host pointer; lr >= 0,
+ * 0 <= beta1 < 1, 0 <= beta2 < 1, eps > 0, weight_decay >= 0, finite
+ * grad_scale, step >= 1.
+ * Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
+ */
+ZR_API zr_status zr_adamw_step(const void *grad, float *master, float *exp_avg, float *exp_avg_sq,
+                        void *param_out, int64_t numel, const zr_adamw_hparams *hp, void *stream);
+
+/* ------------------------------------------------------------- misc ------ */
+
+/* Message for the last failing call on this thread ("" if none). */
+ZR_API const char *zr_last_error(void);
+
+/* ZR_ABI_VERSION of the loaded library. */
+ZR_API int32_t zr_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZR_H */

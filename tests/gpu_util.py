@@ -1,0 +1,103 @@
+"""Helpers for the GPU parity tests: device placement at chosen element
+offsets inside guarded allocations, bit views, and the parity tolerances.
+
+Tolerances (spec parity bar):
+* indexing, layout, pack/unpack, reduce: bit-exact;
+* fp32 master / m / v: |gpu - ref| <= 1e-6 |ref| + 1e-9;
+* bf16 parameter copy: within 1 bf16 ulp (order-mapped integers, +0 == -0).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+GUARD = 64
+GUARD_U16 = 0x5A5A
+GUARD_F32_BITS = 0x7FBADBAD  # a NaN pattern nobody computes
+
+
+def device():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU test run without a visible GPU")
+    return torch.device("cuda:0")
+
+
+def say(*args):
+    print("[gpu-test]", *args, file=sys.stderr, flush=True)
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    """Bits of a 2-byte tensor as numpy uint16."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().contiguous().cpu().numpy().astype(np.float32, copy=False)
+
+
+class Placed:
+    """A device copy of `host` at element `offset` inside a guarded allocation."""
+
+    def __init__(self, host: np.ndarray, offset: int = 0, dev=None):
+        dev = dev or device()
+        n = host.size
+        if host.dtype == np.uint16:
+            big = torch.full((offset + n + GUARD,), GUARD_U16, dtype=torch.int16)
+            big[offset:offset + n] = torch.from_numpy(host.view(np.int16).copy())
+            self.guard_bits = np.uint16(GUARD_U16)
+        elif host.dtype == np.float32:
+            big = torch.from_numpy(np.full(offset + n + GUARD, GUARD_F32_BITS, dtype=np.uint32).view(np.float32))
+            big[offset:offset + n] = torch.from_numpy(host.copy())
+            self.guard_bits = np.uint32(GUARD_F32_BITS)
+        else:
+            raise TypeError(host.dtype)
+        self.big = big.to(dev)
+        self.offset, self.n = offset, n
+        self.view = self.big[offset:offset + n]
+
+    def host(self) -> np.ndarray:
+        if self.view.dtype == torch.int16:
+            return u16(self.view)
+        return f32(self.view)
+
+    def guards_intact(self) -> bool:
+        b = self.big.cpu().numpy()
+        b = b.view(np.uint16) if b.dtype == np.int16 else b.view(np.uint32)
+        return bool(np.all(b[:self.offset] == self.guard_bits) and np.all(b[self.offset + self.n:] == self.guard_bits))
+
+
+def assert_fp32_close(got: np.ndarray, ref: np.ndarray, what: str):
+    g = got.astype(np.float64)
+    r = ref.astype(np.float64)
+    bad = ~(np.abs(g - r) <= 1e-6 * np.abs(r) + 1e-9)
+    if bad.any():
+        i = int(np.flatnonzero(bad)[0])
+        raise AssertionError(f"{what}: {int(bad.sum())} of {got.size} outside 1e-6 rel + 1e-9 abs; "
+                             f"first at {i}: gpu {got[i]!r} oracle {ref[i]!r}")
+
+
+def bf16_order(h: np.ndarray) -> np.ndarray:
+    h = h.astype(np.int64)
+    return np.where(h & 0x8000, -(h & 0x7FFF), h)
+
+
+def assert_bf16_within_1ulp(got: np.ndarray, ref: np.ndarray, what: str):
+    d = np.abs(bf16_order(got) - bf16_order(ref))
+    if (d > 1).any():
+        i = int(np.flatnonzero(d > 1)[0])
+        raise AssertionError(f"{what}: {int((d > 1).sum())} elements beyond 1 bf16 ulp; first at {i}: "
+                             f"gpu {got[i]:#06x} oracle {ref[i]:#06x}")
+
+
+def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str):
+    if got.shape != ref.shape:
+        raise AssertionError(f"{what}: shape {got.shape} vs {ref.shape}")
+    if got.size == 0:
+        return
+    ne = got.view(np.uint8).reshape(got.size, -1) != ref.view(np.uint8).reshape(ref.size, -1)
+    ne = ne.any(axis=1)
+    if ne.any():
+        i = int(np.flatnonzero(ne)[0])
+        raise AssertionError(f"{what}: {int(ne.sum())} of {got.size} differ; first at {i}: "
+                             f"gpu {got[i]!r} oracle {ref[i]!r}")

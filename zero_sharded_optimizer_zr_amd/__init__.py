@@ -1,0 +1,244 @@
+"""Python binding of libzr: one data-parallel rank's share of a ZeRO-3 step on
+an AMD Instinct MI355X.
+
+Argument marshalling only.  Every function has the name of the C entry point
+it calls (declared in ``include/zr.h``); every step of the path runs in the
+library's HIP kernels.  PyTorch provides device memory (``torch.Tensor``) and
+streams.  Importing fails loudly if ``libzr.so`` has not been built.
+
+bf16 buffers may be any 2-byte dtype (torch.bfloat16, torch.int16, ...); their
+bits are passed through unchanged.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence, Tuple, Union
+
+import torch  # loads the process's HIP runtime before libzr binds to it
+
+__all__ = [
+    "ZRError", "Layout", "zr_layout_create", "zr_layout_destroy", "zr_layout_query", "zr_layout_tensor",
+    "zr_layout_rank_range", "zr_layout_fragments", "zr_layout_ledger_bytes", "zr_pack", "zr_unpack",
+    "zr_reduce_slice", "zr_adamw_step", "zr_last_error", "zr_abi_version", "LIBRARY",
+]
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzr.so")
+
+if not os.path.exists(LIBRARY):
+    raise ImportError(f"{LIBRARY} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+
+_lib = ctypes.CDLL(LIBRARY)
+
+ZR_OK, ZR_EINVAL, ZR_ERANGE, ZR_EALIGN, ZR_ENOMEM, ZR_EHIP = range(6)
+_NAMES = {1: "ZR_EINVAL", 2: "ZR_ERANGE", 3: "ZR_EALIGN", 4: "ZR_ENOMEM", 5: "ZR_EHIP"}
+
+
+class ZRError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("psi", ctypes.c_int64), ("psi_part", ctypes.c_int64), ("psi_persist", ctypes.c_int64),
+                ("psi_pad", ctypes.c_int64), ("shard", ctypes.c_int64), ("threshold", ctypes.c_int64),
+                ("n_d", ctypes.c_int32), ("n_tensors", ctypes.c_int32), ("n_partitioned", ctypes.c_int32),
+                ("n_persistent", ctypes.c_int32)]
+
+
+class _Fragment(ctypes.Structure):
+    _fields_ = [("tensor", ctypes.c_int32), ("reserved", ctypes.c_int32), ("tensor_offset", ctypes.c_int64),
+                ("flat_offset", ctypes.c_int64), ("numel", ctypes.c_int64)]
+
+
+class _View(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("first", ctypes.c_int64), ("count", ctypes.c_int64)]
+
+
+class _HParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("grad_scale", ctypes.c_double),
+                ("step", ctypes.c_int64)]
+
+
+_P, _I32, _I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_SIGS = {
+    "zr_layout_create": ([_P, _I32, _I32, _I64, _P], _I32),
+    "zr_layout_destroy": ([_P], None),
+    "zr_layout_query": ([_P, _P], _I32),
+    "zr_layout_tensor": ([_P, _I32, _P, _P], _I32),
+    "zr_layout_rank_range": ([_P, _I32, _P, _P], _I32),
+    "zr_layout_fragments": ([_P, _I64, _I64, _P, _I32, _P], _I32),
+    "zr_layout_ledger_bytes": ([_P, _I32, _P], _I32),
+    "zr_pack": ([_P, _P, _I32, _P, _I64, _I64, _P], _I32),
+    "zr_unpack": ([_P, _P, _I64, _I64, _P, _I32, _P], _I32),
+    "zr_reduce_slice": ([_P, _I32, _I64, _P, _P], _I32),
+    "zr_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _P], _I32),
+    "zr_last_error": ([], ctypes.c_char_p),
+    "zr_abi_version": ([], _I32),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+SYMBOLS = tuple(_SIGS)
+
+
+def zr_last_error() -> str:
+    return _lib.zr_last_error().decode()
+
+
+def zr_abi_version() -> int:
+    return _lib.zr_abi_version()
+
+
+def _check(status: int):
+    if status != ZR_OK:
+        raise ZRError(status, zr_last_error())
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: Optional[torch.Tensor], size: int, name: str) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.element_size() != size:
+        raise TypeError(f"{name} must have {size}-byte elements")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() or None
+
+
+# ---------------------------------------------------------------- layout ----
+
+class Layout:
+    """Owns a zr_layout handle (released on garbage collection)."""
+
+    def __init__(self, handle: int, numels: Sequence[int]):
+        self._h = ctypes.c_void_p(handle)
+        self.numels = list(numels)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value:
+            _lib.zr_layout_destroy(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def info(self) -> dict:
+        return zr_layout_query(self)
+
+
+def zr_layout_create(numels: Sequence[int], n_d: int, persist_threshold: int = 100_000) -> Layout:
+    arr = (ctypes.c_int64 * max(1, len(numels)))(*[int(x) for x in numels])
+    out = ctypes.c_void_p()
+    _check(_lib.zr_layout_create(arr, len(numels), int(n_d), int(persist_threshold), ctypes.byref(out)))
+    return Layout(out.value, numels)
+
+
+def zr_layout_destroy(layout: Layout) -> None:
+    layout.__del__()
+
+
+def zr_layout_query(layout: Layout) -> dict:
+    info = _Info()
+    _check(_lib.zr_layout_query(layout.handle, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in _Info._fields_}
+
+
+def zr_layout_tensor(layout: Layout, t: int) -> Tuple[bool, int]:
+    p, off = ctypes.c_int32(), ctypes.c_int64()
+    _check(_lib.zr_layout_tensor(layout.handle, int(t), ctypes.byref(p), ctypes.byref(off)))
+    return bool(p.value), off.value
+
+
+def zr_layout_rank_range(layout: Layout, rank: int) -> Tuple[int, int]:
+    b, e = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.zr_layout_rank_range(layout.handle, int(rank), ctypes.byref(b), ctypes.byref(e)))
+    return b.value, e.value
+
+
+def zr_layout_fragments(layout: Layout, begin: int, end: int) -> List[Tuple[int, int, int, int]]:
+    """(tensor, tensor_offset, flat_offset, numel) of every piece in [begin, end)."""
+    n = ctypes.c_int32()
+    status = _lib.zr_layout_fragments(layout.handle, int(begin), int(end), None, 0, ctypes.byref(n))
+    if status not in (ZR_OK, ZR_ERANGE) or (status == ZR_ERANGE and n.value == 0):
+        _check(status)
+    buf = (_Fragment * max(1, n.value))()
+    _check(_lib.zr_layout_fragments(layout.handle, int(begin), int(end), buf, n.value, ctypes.byref(n)))
+    return [(f.tensor, f.tensor_offset, f.flat_offset, f.numel) for f in buf[:n.value]]
+
+
+def zr_layout_ledger_bytes(layout: Layout, stage: int) -> int:
+    out = ctypes.c_int64()
+    _check(_lib.zr_layout_ledger_bytes(layout.handle, int(stage), ctypes.byref(out)))
+    return out.value
+
+
+# ----------------------------------------------------------- pack/unpack ----
+
+ViewArg = Union[None, torch.Tensor, Tuple[torch.Tensor, int]]
+
+
+def _views(layout: Layout, views: Sequence[ViewArg]):
+    arr = (_View * max(1, len(views)))()
+    for t, v in enumerate(views):
+        if v is None:
+            continue
+        tensor, first = (v, 0) if isinstance(v, torch.Tensor) else v
+        arr[t].ptr = _ptr(tensor, 2, f"views[{t}]")
+        arr[t].first = int(first)
+        arr[t].count = tensor.numel()
+    return arr
+
+
+def zr_pack(layout: Layout, views: Sequence[ViewArg], flat: torch.Tensor, begin: int, end: int,
+            stream=None) -> None:
+    """flat (holding flat elements [begin, end)) <- per-tensor views; padding zeroed.
+    views[t] is None, a tensor holding all of tensor t, or (tensor, first)."""
+    _check(_lib.zr_pack(layout.handle, _views(layout, views), len(views), _ptr(flat, 2, "flat"),
+                        int(begin), int(end), _stream(stream)))
+
+
+def zr_unpack(layout: Layout, flat: torch.Tensor, begin: int, end: int, views: Sequence[ViewArg],
+              stream=None) -> None:
+    """per-tensor views <- flat elements [begin, end)."""
+    _check(_lib.zr_unpack(layout.handle, _ptr(flat, 2, "flat"), int(begin), int(end),
+                          _views(layout, views), len(views), _stream(stream)))
+
+
+# ------------------------------------------------------------ reduce/adamw ----
+
+def zr_reduce_slice(contribs: Sequence[torch.Tensor], out: torch.Tensor, numel: Optional[int] = None,
+                    stream=None) -> None:
+    """out[i] = bf16(mean over k of contribs[k][i]) for i < numel (default out.numel())."""
+    n = len(contribs)
+    table = (ctypes.c_void_p * max(1, n))(*[_ptr(c, 2, f"contribs[{k}]") for k, c in enumerate(contribs)])
+    numel = out.numel() if numel is None else int(numel)
+    _check(_lib.zr_reduce_slice(table, n, numel, _ptr(out, 2, "out"), _stream(stream)))
+
+
+def zr_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                  param_out: Optional[torch.Tensor], *, lr: float, beta1: float, beta2: float, eps: float,
+                  weight_decay: float, step: int, grad_scale: float = 1.0, numel: Optional[int] = None,
+                  stream=None) -> None:
+    """In-place AdamW on fp32 master/exp_avg/exp_avg_sq from a bf16 gradient, with
+    the bf16 copy of the new master written to param_out (unless None)."""
+    hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
+                  int(step))
+    numel = master.numel() if numel is None else int(numel)
+    _check(_lib.zr_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                              _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
+                              ctypes.byref(hp), _stream(stream)))

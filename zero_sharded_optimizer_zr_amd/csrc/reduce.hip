@@ -1,0 +1,196 @@
+// Local arithmetic of the gradient ReduceScatter on one rank's slice (gfx950):
+// out = bf16(mean of n bf16 contributions), summed in fp32 in ascending
+// contribution order, divided once by n, rounded to nearest even.
+//
+// Per element: n two-byte reads and one two-byte write, a few fp32 adds: bound
+// by HBM bandwidth at (2n + 2) bytes per element.  Each lane takes 8
+// consecutive elements (one 16-byte load per contribution, one 16-byte store)
+// over a grid-stride loop; contribution loads are issued four at a time so
+// several 16-byte reads are in flight per lane.  The n device pointers travel by
+// value in the kernel arguments.  No LDS.
+//
+// Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
+// blog (111qqz.com), "ZeRO-2: why gradients can be sharded too" (ReduceScatter
+// leaves rank r with slice r of the averaged gradient: [2,6] and [4,10] give
+// [3] and [8]) and its ledger section (bf16 gradients); ZeRO-1/2/3 concept page
+// (compassingai.com), Stage 2 and Stage 3 mechanism.
+#include <algorithm>
+
+#include "zr_device.hpp"
+#include "zr_internal.hpp"
+
+namespace zr {
+
+#ifndef ZR_REDUCE_BLOCKS_PER_CU
+#define ZR_REDUCE_BLOCKS_PER_CU 8
+#endif
+
+constexpr int kMaxContribs = 256;
+
+template <int MaxN>
+struct ContribTable {
+    const uint16_t *p[MaxN];
+};
+
+struct MeanDivisor {
+    float n;      // (float)n
+    float inv;    // 1/n, exact when n is a power of two
+    int32_t pow2; // multiply by inv (same bits as dividing by n) instead of dividing
+};
+
+__device__ __forceinline__ float finish_mean(float sum, const MeanDivisor &d)
+{
+    return d.pow2 ? sum * d.inv : __fdiv_rn(sum, d.n);
+}
+
+__device__ __forceinline__ void add8(float (&acc)[8], u32x4 x)
+{
+    acc[0] += bf16_lo(x.x);
+    acc[1] += bf16_hi(x.x);
+    acc[2] += bf16_lo(x.y);
+    acc[3] += bf16_hi(x.y);
+    acc[4] += bf16_lo(x.z);
+    acc[5] += bf16_hi(x.z);
+    acc[6] += bf16_lo(x.w);
+    acc[7] += bf16_hi(x.w);
+}
+
+template <int MaxN>
+__device__ __forceinline__ uint16_t reduce_one(const ContribTable<MaxN> &c, int32_t n, int64_t j,
+                                               const MeanDivisor &d)
+{
+    float sum = bf16_to_f32(c.p[0][j]);
+    for (int32_t k = 1; k < n; ++k)
+        sum += bf16_to_f32(c.p[k][j]);
+    return (uint16_t)f32_to_bf16(finish_mean(sum, d));
+}
+
+// Vector body over `groups` groups of 8 elements from element `head` (where
+// every contribution and the output are 16-byte aligned); block 0 also does
+// the unaligned head [0, head) and the tail element-wise.  out may be
+// c.p[0]: each lane reads all its inputs before it writes.
+template <int MaxN>
+__global__ __launch_bounds__(kBlock) void reduce_vec_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
+                                                            int64_t numel, int64_t head, int64_t groups,
+                                                            MeanDivisor d)
+{
+    u32x4 *o4 = reinterpret_cast<u32x4 *>(out + head);
+    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+        float acc[8];
+        {
+            u32x4 x = reinterpret_cast<const u32x4 *>(c.p[0] + head)[i];
+            acc[0] = bf16_lo(x.x);
+            acc[1] = bf16_hi(x.x);
+            acc[2] = bf16_lo(x.y);
+            acc[3] = bf16_hi(x.y);
+            acc[4] = bf16_lo(x.z);
+            acc[5] = bf16_hi(x.z);
+            acc[6] = bf16_lo(x.w);
+            acc[7] = bf16_hi(x.w);
+        }
+        int32_t k = 1;
+        for (; k + 4 <= n; k += 4) {
+            u32x4 x0 = reinterpret_cast<const u32x4 *>(c.p[k] + head)[i];
+            u32x4 x1 = reinterpret_cast<const u32x4 *>(c.p[k + 1] + head)[i];
+            u32x4 x2 = reinterpret_cast<const u32x4 *>(c.p[k + 2] + head)[i];
+            u32x4 x3 = reinterpret_cast<const u32x4 *>(c.p[k + 3] + head)[i];
+            add8(acc, x0);
+            add8(acc, x1);
+            add8(acc, x2);
+            add8(acc, x3);
+        }
+        for (; k < n; ++k)
+            add8(acc, reinterpret_cast<const u32x4 *>(c.p[k] + head)[i]);
+        u32x4 r;
+        r.x = pack_bf16x2(finish_mean(acc[0], d), finish_mean(acc[1], d));
+        r.y = pack_bf16x2(finish_mean(acc[2], d), finish_mean(acc[3], d));
+        r.z = pack_bf16x2(finish_mean(acc[4], d), finish_mean(acc[5], d));
+        r.w = pack_bf16x2(finish_mean(acc[6], d), finish_mean(acc[7], d));
+        o4[i] = r;
+    }
+    if (blockIdx.x == 0) {
+        int64_t tail_start = head + 8 * groups;
+        int64_t edge = head + (numel - tail_start);
+        if ((int64_t)threadIdx.x < edge) {
+            int64_t j = (int64_t)threadIdx.x < head ? (int64_t)threadIdx.x : tail_start + (threadIdx.x - head);
+            out[j] = reduce_one(c, n, j, d);
+        }
+    }
+}
+
+// Fallback when the buffers' 16-byte phases disagree: element-wise, same bits.
+template <int MaxN>
+__global__ __launch_bounds__(kBlock) void reduce_scalar_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
+                                                               int64_t numel, MeanDivisor d)
+{
+    for (int64_t j = global_tid(); j < numel; j += grid_stride())
+        out[j] = reduce_one(c, n, j, d);
+}
+
+int device_cu_count();
+
+template <int MaxN>
+static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t numel, uint16_t *out,
+                               hipStream_t st, const MeanDivisor &d)
+{
+    ContribTable<MaxN> c = {};
+    for (int32_t k = 0; k < n; ++k)
+        c.p[k] = static_cast<const uint16_t *>(contribs[k]);
+    const int64_t max_blocks = (int64_t)device_cu_count() * ZR_REDUCE_BLOCKS_PER_CU;
+    int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(out) & 15)) & 15) / 2);
+    if (head > numel)
+        head = numel;
+    bool vec = true;
+    for (int32_t k = 0; k < n && vec; ++k)
+        vec = aligned_to(c.p[k] + head, 16);
+    if (vec) {
+        int64_t groups = (numel - head) / 8;
+        int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((groups + kBlock - 1) / kBlock, max_blocks));
+        return launch(reduce_vec_kernel<MaxN>, dim3((unsigned)blocks), dim3(kBlock), st, c, n, out, numel, head,
+                      groups, d);
+    }
+    int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((numel + kBlock - 1) / kBlock, max_blocks));
+    return launch(reduce_scalar_kernel<MaxN>, dim3((unsigned)blocks), dim3(kBlock), st, c, n, out, numel, d);
+}
+
+}  // namespace zr
+
+using namespace zr;
+
+extern "C" zr_status zr_reduce_slice(const void *const *contribs, int32_t n, int64_t numel, void *out, void *stream)
+{
+    clear_error();
+    if (!contribs)
+        return fail(ZR_EINVAL, "zr_reduce_slice: contribs is NULL");
+    if (n < 1 || n > kMaxContribs)
+        return fail(ZR_EINVAL, "zr_reduce_slice: n = %d outside [1, %d]", n, kMaxContribs);
+    if (numel < 0)
+        return fail(ZR_EINVAL, "zr_reduce_slice: numel < 0");
+    if (numel > 0 && !out)
+        return fail(ZR_EINVAL, "zr_reduce_slice: out is NULL");
+    if (!aligned_to(out, 2))
+        return fail(ZR_EALIGN, "zr_reduce_slice: out must be 2-byte aligned");
+    for (int32_t k = 0; k < n; ++k) {
+        if (numel > 0 && !contribs[k])
+            return fail(ZR_EINVAL, "zr_reduce_slice: contribs[%d] is NULL", k);
+        if (!aligned_to(contribs[k], 2))
+            return fail(ZR_EALIGN, "zr_reduce_slice: contribs[%d] must be 2-byte aligned", k);
+        bool same = contribs[k] == out;
+        if (!(k == 0 && same) && overlaps(contribs[k], 2 * numel, out, 2 * numel))
+            return fail(ZR_EINVAL, "zr_reduce_slice: out overlaps contribs[%d] (only out == contribs[0] is allowed)", k);
+    }
+    if (numel == 0)
+        return ZR_OK;
+
+    MeanDivisor d;
+    d.n = (float)n;
+    d.inv = 1.0f / (float)n;
+    d.pow2 = (n & (n - 1)) == 0;
+    auto o = static_cast<uint16_t *>(out);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n <= 8)
+        return reduce_launch<8>(contribs, n, numel, o, st, d);
+    if (n <= 64)
+        return reduce_launch<64>(contribs, n, numel, o, st, d);
+    return reduce_launch<kMaxContribs>(contribs, n, numel, o, st, d);
+}

@@ -1,0 +1,39 @@
+// Device helpers shared by the gfx950 kernels of libzr.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace zr {
+
+// Native clang vectors: one 16-byte global access per lane (global_load/store_dwordx4).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlock = 256;  // 4 wave64 per workgroup
+
+// bf16 -> fp32 is exact: the 16 bits are the upper half of the fp32 pattern.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even on the upper half; NaN stays NaN
+// (sign and upper payload kept, quiet bit set).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Global thread index and stride over a 1-D grid, 64-bit.
+__device__ __forceinline__ int64_t global_tid() { return (int64_t)blockIdx.x * blockDim.x + threadIdx.x; }
+__device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * blockDim.x; }
+
+}  // namespace zr

@@ -1,0 +1,61 @@
+// Host-side internals shared by the translation units of libzr.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <functional>
+#include <tuple>
+#include <utility>
+#include <vector>
+
+#include "zr.h"
+
+struct zr_layout {
+    std::vector<int64_t> numel;       // per tensor
+    std::vector<int64_t> offset;      // flat offset, or offset in the persistent region
+    std::vector<uint8_t> persistent;  // per tensor
+    // non-empty partitioned tensors in flat order, for range queries
+    std::vector<int32_t> part_tensor;
+    std::vector<int64_t> part_begin;
+    int64_t psi = 0, psi_part = 0, psi_persist = 0, psi_pad = 0, shard = 0, threshold = 0;
+    int32_t n_d = 1, n_tensors = 0, n_partitioned = 0, n_persistent = 0;
+};
+
+namespace zr {
+
+// Records a message for zr_last_error() on this thread and returns `status`.
+zr_status fail(zr_status status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Enumerates the fragments of [begin, end) (range already validated).
+void for_each_fragment(const zr_layout &L, int64_t begin, int64_t end,
+                       const std::function<void(const zr_fragment &)> &fn);
+
+inline bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+inline bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
+{
+    auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return abytes > 0 && bbytes > 0 && x < y + static_cast<uintptr_t>(bbytes) &&
+           y < x + static_cast<uintptr_t>(abytes);
+}
+
+// Launches `kernel` through hipLaunchKernel so the status of this launch is
+// returned directly (no sticky-error ambiguity).
+template <typename... Params, typename... Args>
+zr_status launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream, Args &&...args)
+{
+    std::tuple<Params...> values(std::forward<Args>(args)...);
+    void *ptrs[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
+    std::apply([&](auto &...v) {
+        int i = 0;
+        ((ptrs[i++] = static_cast<void *>(&v)), ...);
+    }, values);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+    if (e != hipSuccess)
+        return fail(ZR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ZR_OK;
+}
+
+}  // namespace zr
