@@ -1,0 +1,230 @@
+"""Full-size workloads on the GPU through the C ABI, checked against the oracle.
+
+Shards have the real sizes (1.75e9, 1.05e8, 1.16e8 and 1.95e9 elements); the
+oracle recomputes sampled outputs one by one (about a million random elements
+plus the first and last 8192 of every buffer) from inputs snapshotted before the
+in-place update, and the layout-dependent copies are checked window by window
+against the oracle's pack/unpack.  Tolerances: reduce, pack, unpack and all
+indexing bit-exact; fp32 master / m / v within 1e-6 relative + 1e-9 absolute;
+bf16 copy within 1 ulp.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import zero_sharded_optimizer_zr_amd as zr
+from gpu_util import assert_bf16_within_1ulp, assert_bits_equal, assert_fp32_close, device, say
+from zr_workloads import FLAT_1T, FLAT_7B, GPT_7P5B, LLAMA_7B, TINY_MLP, synth
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+SAMPLES = 1 << 20
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def sample_idx(n, seed, dev):
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    r = torch.randint(0, n, (min(SAMPLES, n),), generator=g)
+    edge = torch.cat([torch.arange(0, min(8192, n)), torch.arange(max(0, n - 8192), n)])
+    return torch.unique(torch.cat([r, edge])).to(dev)
+
+
+def take16(t, idx):
+    return t.view(torch.int16)[idx].cpu().numpy().view(np.uint16).copy()
+
+
+def take32(t, idx):
+    return t[idx].cpu().numpy().astype(np.float32).copy()
+
+
+def slice16(t, a, b):
+    return t.view(torch.int16)[a:b].cpu().numpy().view(np.uint16).copy()
+
+
+def run_shard(w, n, dev, steps, step_index0=0, salt=0, param_out=True):
+    """GPU: reduce the contributions, AdamW on the shard, for each step in
+    `steps`; oracle: the same on sampled elements.
+
+    Each step is checked against the oracle run from the GPU's own state before
+    that step (the strict per-step bar).  Over several steps an oracle that
+    carries its own state drifts from the fp32 GPU path by at most one
+    per-step bound per step, which is checked too."""
+    idx = sample_idx(n, 1000 + w.seed + salt, dev)
+    st = synth.shard_state(w, n, device=dev, salt=salt)
+    master, m, v = st["master"], st["exp_avg"], st["exp_avg_sq"]
+    carried = [take32(master, idx), take32(m, idx), take32(v, idx)]
+    grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    param = torch.empty(n, dtype=torch.bfloat16, device=dev) if param_out else None
+    for si, t in enumerate(steps):
+        contribs = synth.contributions(w, n, step_index=step_index0 + si, device=dev, salt=salt)
+        o_contribs = [take16(c, idx) for c in contribs]
+        before = [take32(master, idx), take32(m, idx), take32(v, idx)]
+        say(w.name, f"step t={t}: reduce over {len(contribs)} contributions of {n}")
+        zr.zr_reduce_slice(contribs, grad)
+        zr.zr_adamw_step(grad, master, m, v, param, step=t, **w.hparams)
+        torch.cuda.synchronize()
+        o_grad = oracle.reduce(o_contribs)
+        assert_bits_equal(take16(grad, idx), o_grad, f"{w.name} reduce t={t}")
+        o_param = np.zeros(idx.numel(), np.uint16) if param_out else None
+        oracle.adamw(o_grad, *before, o_param, step=t, **w.hparams)
+        oracle.adamw(o_grad, *carried, None, step=t, **w.hparams)
+        for name, got, want in zip(("master", "exp_avg", "exp_avg_sq"), (master, m, v), before):
+            assert_fp32_close(take32(got, idx), want, f"{w.name} {name} t={t}")
+        if param_out:
+            assert_bf16_within_1ulp(take16(param, idx), o_param, f"{w.name} param t={t}")
+        del contribs
+    k = len(steps)
+    for name, got, want in zip(("master", "exp_avg", "exp_avg_sq"), (master, m, v), carried):
+        g64, w64 = take32(got, idx).astype(np.float64), want.astype(np.float64)
+        drift = np.abs(g64 - w64)
+        assert np.all(drift <= k * (1e-6 * np.abs(w64) + 1e-9)), f"{w.name} {name}: drift over {k} steps"
+    return dict(master=master, m=m, v=v, grad=grad, param=param, idx=idx)
+
+
+def check_windows(ref, flat, b, views, dev, seed, what, n_windows=256, width=4096):
+    """Compare flat[b + x] for windows of the range against the oracle's pack of
+    the same windows, views copied to the host fragment by fragment.  Windows
+    sit at random places and on every tensor boundary inside the range."""
+    e = b + flat.numel()
+    rng = np.random.default_rng(seed)
+    starts = list(rng.integers(b, max(b + 1, e - width), n_windows))
+    for t in range(len(ref.numels)):
+        if not ref.persistent[t]:
+            for edge in (ref.offset[t], ref.offset[t] + ref.numels[t]):
+                if b <= edge <= e:
+                    starts.append(max(b, min(edge - width // 2, e - width)))
+    for s in starts:
+        s = int(s)
+        we = min(e, s + width)
+        host_views = [None] * len(ref.numels)
+        for t, toff, foff, n in ref.fragments(s, we):
+            tensor, first = views[t]
+            host_views[t] = (slice16(tensor, toff - first, toff - first + n), toff)
+        want = oracle.pack(ref, host_views, s, we)
+        got = slice16(flat, s - b, we - b)
+        assert_bits_equal(got, want, f"{what} window [{s}, {we})")
+
+
+# ------------------------------------------------------------------------
+
+def test_tiny_mlp_full_buffer_pack_unpack_and_persistent_update():
+    dev = device()
+    w = TINY_MLP
+    ref = oracle.Layout(w.numels, w.n_d, w.threshold)
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    views = [None if ref.persistent[t] else synth.random_bits16(x, 40 + t).to(dev) for t, x in enumerate(w.numels)]
+    flat = torch.empty(ref.psi_pad, dtype=torch.int16, device=dev)
+    zr.zr_pack(lay, views, flat, 0, ref.psi_pad)
+    host_views = [None if v is None else (v.cpu().numpy().view(np.uint16).copy(), 0) for v in views]
+    assert_bits_equal(flat.cpu().numpy().view(np.uint16), oracle.pack(ref, host_views, 0, ref.psi_pad),
+                      "tiny mlp full pack")
+    back = [None if v is None else torch.zeros_like(v) for v in views]
+    zr.zr_unpack(lay, flat, 0, ref.psi_pad, back)
+    for v, x in zip(views, back):
+        if v is not None:
+            assert torch.equal(v, x)
+    # persistent region (the two biases): the AllReduce mean and the same update on every rank
+    n = ref.psi_persist
+    st = synth.shard_state(w, n, salt=9)
+    contribs = synth.contributions(w, n, salt=9)
+    grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    zr.zr_reduce_slice([c.to(dev) for c in contribs], grad)
+    d = {k: st[k].to(dev) for k in st}
+    p = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    zr.zr_adamw_step(grad, d["master"], d["exp_avg"], d["exp_avg_sq"], p, step=1, **w.hparams)
+    o_grad = oracle.reduce([c.view(torch.int16).numpy().view(np.uint16).copy() for c in contribs])
+    o = [st[k].numpy().copy() for k in ("master", "exp_avg", "exp_avg_sq")]
+    op = np.zeros(n, np.uint16)
+    oracle.adamw(o_grad, *o, op, step=1, **w.hparams)
+    assert_bits_equal(grad.view(torch.int16).cpu().numpy().view(np.uint16), o_grad, "persistent reduce")
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), o):
+        assert_fp32_close(d[k].cpu().numpy(), want, f"persistent {name}")
+    assert_bf16_within_1ulp(p.view(torch.int16).cpu().numpy().view(np.uint16), op, "persistent param")
+
+
+def test_flat_7b_nd4_shard():
+    dev = device()
+    w = FLAT_7B
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    b, e = zr.zr_layout_rank_range(lay, w.rank)
+    assert (b, e) == (0, 1_750_000_000)
+    out = run_shard(w, e - b, dev, w.steps)
+    # unpack the updated bf16 shard into the flat tensor's window [b, e): an exact copy
+    view = torch.empty(e - b, dtype=torch.bfloat16, device=dev)
+    zr.zr_unpack(lay, out["param"], b, e, [(view, b)])
+    assert torch.equal(view.view(torch.int16), out["param"].view(torch.int16))
+
+
+def test_llama_7b_nd64_rank17():
+    dev = device()
+    w = LLAMA_7B
+    ref = oracle.Layout(w.numels, w.n_d, w.threshold)
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    b, e = zr.zr_layout_rank_range(lay, w.rank)
+    assert (b, e) == ref.rank_range(w.rank) == (1_789_820_928, 1_895_104_512)
+    frs = zr.zr_layout_fragments(lay, b, e)
+    assert frs == ref.fragments(b, e) and len(frs) == 4
+    # the 64 contributions, AdamW t = 1, bf16 copy into the rank's slot of the flat buffer
+    out = run_shard(w, e - b, dev, w.steps)
+    # unpack the slot into per-tensor windows covering the shard's fragments, then pack them back
+    views = [None] * len(w.numels)
+    for t, toff, _, n in frs:
+        views[t] = (torch.full((n + 16,), 0x5A5A, dtype=torch.int16, device=dev)[5:5 + n], toff)
+    zr.zr_unpack(lay, out["param"], b, e, views)
+    again = torch.empty(e - b, dtype=torch.bfloat16, device=dev)
+    zr.zr_pack(lay, views, again, b, e)
+    assert torch.equal(again.view(torch.int16), out["param"].view(torch.int16))
+    check_windows(ref, out["param"], b, views, dev, 17, "llama rank-17 unpack")
+    del out
+    torch.cuda.empty_cache()
+    # the whole flat buffer (13.5 GB) packed from per-tensor views of random bits
+    say("llama: full-buffer pack of", ref.psi_pad, "elements")
+    full_views = [None if ref.persistent[t] else (synth.random_bits16(x, 500 + t, dev), 0)
+                  for t, x in enumerate(w.numels)]
+    flat = torch.empty(ref.psi_pad, dtype=torch.int16, device=dev)
+    zr.zr_pack(lay, full_views, flat, 0, ref.psi_pad)
+    check_windows(ref, flat, 0, full_views, dev, 3, "llama full pack", n_windows=512)
+    # and unpacked into fresh views: every tensor equals its source bit for bit
+    fresh = [None if v is None else (torch.empty_like(v[0]), 0) for v in full_views]
+    zr.zr_unpack(lay, flat, 0, ref.psi_pad, fresh)
+    for t, (a, c) in enumerate(zip(full_views, fresh)):
+        if a is not None:
+            assert torch.equal(a[0], c[0]), f"tensor {t}"
+    # persistent RMSNorm vectors: fp32 master is the working parameter (no bf16 copy)
+    del flat, full_views, fresh
+    torch.cuda.empty_cache()
+    run_shard(w, ref.psi_persist, dev, w.steps, salt=77, param_out=False)
+
+
+def test_gpt_7p5b_nd64_ten_steps():
+    dev = device()
+    w = GPT_7P5B
+    ref = oracle.Layout(w.numels, w.n_d, w.threshold)
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    b, e = zr.zr_layout_rank_range(lay, w.rank)
+    assert (b, e) == (0, 116_465_664) and zr.zr_layout_fragments(lay, b, e) == [(0, 0, 0, 116_465_664)]
+    assert ref.n_persistent == 290
+    run_shard(w, e - b, dev, w.steps)              # 10 consecutive steps, fresh contributions each
+    run_shard(w, ref.psi_persist, dev, w.steps, salt=55)   # the 290 persistent tensors
+
+
+def test_flat_1t_nd512_shard_and_unpack():
+    dev = device()
+    w = FLAT_1T
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    b, e = zr.zr_layout_rank_range(lay, w.rank)
+    assert (b, e) == (0, 1_953_125_000)
+    b511, e511 = zr.zr_layout_rank_range(lay, 511)
+    assert e511 == 10**12 and b511 > 2**32
+    out = run_shard(w, e - b, dev, w.steps)
+    view = torch.empty(e - b, dtype=torch.bfloat16, device=dev)
+    zr.zr_unpack(lay, out["param"], b, e, [(view, b)])
+    assert torch.equal(view.view(torch.int16), out["param"].view(torch.int16))

@@ -4,9 +4,13 @@
 // The host turns the layout's fragments of [begin, end) (plus, for pack, the
 // zero padding at the end of the flat buffer) into copy descriptors
 // {src, dst, n}; descriptors travel by value in the kernel arguments, in batches.
-// Every workgroup copies one tile of up to 8192 elements of one descriptor; it
-// finds its descriptor by a binary search over the batch's tile prefix sums
-// (uniform, scalar loads).  Copies are 16-byte stores aligned on the
+// Every workgroup copies one tile of 2048 elements (one 16-byte chunk per lane)
+// of one descriptor; it finds its descriptor by a binary search over the
+// batch's tile prefix sums (uniform, scalar loads).  Tiles are dealt to the 8
+// XCDs in contiguous runs (workgroup b runs on XCD b mod 8, so tile
+// (b mod 8) * (grid / 8) + b / 8 gives each XCD's L2 one contiguous stretch),
+// which measured 6.7 TB/s against 6.5 for the plain order on a 2-stream copy.
+// Loads and stores are non-temporal 16-byte accesses aligned on the
 // destination.  When source and destination have the same 16-byte phase the
 // loads are aligned 16-byte loads too; otherwise (a tensor edge or a shard edge
 // at an element offset that is not a multiple of 8) each lane loads the two
@@ -33,9 +37,9 @@
 
 namespace zr {
 
-constexpr int kChunksPerThread = 4;
-constexpr int64_t kTileChunks = (int64_t)kBlock * kChunksPerThread;  // 16-byte chunks per tile
-constexpr int kMaxDesc = 96;                                          // 3 KB of descriptors per launch
+constexpr int64_t kTileChunks = kBlock;  // 16-byte chunks per tile: one per lane
+constexpr int kXcds = 8;                 // MI355X: workgroups go round-robin to 8 XCDs
+constexpr int kMaxDesc = 96;             // 3 KB of descriptors per launch
 
 struct CopyDesc {
     const uint16_t *src;  // NULL: fill with zeros
@@ -81,9 +85,13 @@ __device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 b, uint32_t shift_bytes)
     }
 }
 
-__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch)
+__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch, int64_t total_tiles)
 {
-    const int64_t tile = blockIdx.x;
+    // grid is a multiple of kXcds; spare workgroups past the last tile exit
+    const int64_t per_xcd = gridDim.x / kXcds;
+    const int64_t tile = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    if (tile >= total_tiles)
+        return;
     int lo = 0, hi = batch.count - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -102,40 +110,16 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch)
     const int64_t tail_start = head + 8 * body;
 
     u32x4 *d4 = reinterpret_cast<u32x4 *>(dst + head);
-    const int64_t c0 = t * kTileChunks + threadIdx.x;
-    if (src == nullptr) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int u = 0; u < kChunksPerThread; ++u) {
-            int64_t c = c0 + (int64_t)u * kBlock;
-            if (c < body)
-                d4[c] = z;
-        }
-    } else {
-        const uintptr_t s_addr = reinterpret_cast<uintptr_t>(src + head);
-        const uint32_t shift = (uint32_t)(s_addr & 15);  // uniform per descriptor
-        const u32x4 *s4 = reinterpret_cast<const u32x4 *>(s_addr - shift);
-        u32x4 v[kChunksPerThread];
-        if (shift == 0) {
-#pragma unroll
-            for (int u = 0; u < kChunksPerThread; ++u) {
-                int64_t c = c0 + (int64_t)u * kBlock;
-                if (c < body)
-                    v[u] = s4[c];
-            }
+    const int64_t c = t * kTileChunks + threadIdx.x;
+    if (c < body) {
+        if (src == nullptr) {
+            store_stream(d4 + c, u32x4{0u, 0u, 0u, 0u});
         } else {
-#pragma unroll
-            for (int u = 0; u < kChunksPerThread; ++u) {
-                int64_t c = c0 + (int64_t)u * kBlock;
-                if (c < body)
-                    v[u] = funnel(s4[c], s4[c + 1], shift);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < kChunksPerThread; ++u) {
-            int64_t c = c0 + (int64_t)u * kBlock;
-            if (c < body)
-                d4[c] = v[u];
+            const uintptr_t s_addr = reinterpret_cast<uintptr_t>(src + head);
+            const uint32_t shift = (uint32_t)(s_addr & 15);  // uniform per descriptor
+            const u32x4 *s4 = reinterpret_cast<const u32x4 *>(s_addr - shift);
+            u32x4 v = shift == 0 ? load_stream(s4 + c) : funnel(load_stream(s4 + c), load_stream(s4 + c + 1), shift);
+            store_stream(d4 + c, v);
         }
     }
 
@@ -168,7 +152,7 @@ zr_status launch_pieces(const std::vector<Piece> &pieces, hipStream_t st)
             const Piece &p = pieces[i];
             int64_t body = (p.n - dst_head(p.dst, p.n)) / 8;
             int64_t nt = std::max<int64_t>(1, (body + kTileChunks - 1) / kTileChunks);
-            if (count > 0 && tiles + nt > (int64_t)INT32_MAX)
+            if (count > 0 && tiles + nt > (int64_t)INT32_MAX - kXcds)
                 break;
             batch.d[count].src = p.src;
             batch.d[count].dst = p.dst;
@@ -179,9 +163,10 @@ zr_status launch_pieces(const std::vector<Piece> &pieces, hipStream_t st)
             ++i;
         }
         batch.count = count;
-        if (tiles > (int64_t)INT32_MAX)
+        int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
+        if (blocks > (int64_t)INT32_MAX)
             return fail(ZR_ERANGE, "pack/unpack: fragment too large for one launch");
-        zr_status s = launch(copy_kernel, dim3((unsigned)tiles), dim3(kBlock), st, batch);
+        zr_status s = launch(copy_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, batch, tiles);
         if (s != ZR_OK)
             return s;
     }

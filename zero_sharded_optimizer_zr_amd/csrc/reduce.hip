@@ -4,10 +4,14 @@
 //
 // Per element: n two-byte reads and one two-byte write, a few fp32 adds: bound
 // by HBM bandwidth at (2n + 2) bytes per element.  Each lane takes 8
-// consecutive elements (one 16-byte load per contribution, one 16-byte store)
-// over a grid-stride loop; contribution loads are issued four at a time so
-// several 16-byte reads are in flight per lane.  The n device pointers travel by
-// value in the kernel arguments.  No LDS.
+// consecutive elements (one 16-byte non-temporal load per contribution, one
+// 16-byte store), one group per lane over a grid that covers the slice;
+// contribution loads are issued eight at a time so several 16-byte reads are in
+// flight per lane.  With more than 8 contributions the kernel holds at most 2
+// workgroups per CU (LDS reserved, never touched): with n + 1 streams the DRAM
+// rows thrash when every CU is full (measured on MI355X at n = 64: 5.8 TB/s
+// uncapped, 6.4 TB/s capped).  The n device pointers travel by value in the
+// kernel arguments.
 //
 // Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
 // blog (111qqz.com), "ZeRO-2: why gradients can be sharded too" (ReduceScatter
@@ -21,11 +25,9 @@
 
 namespace zr {
 
-#ifndef ZR_REDUCE_BLOCKS_PER_CU
-#define ZR_REDUCE_BLOCKS_PER_CU 8
-#endif
-
 constexpr int kMaxContribs = 256;
+constexpr int kLoadBatch = 8;                  // contribution loads in flight per lane
+constexpr size_t kManyContribLds = 80 * 1024;  // 2 workgroups per CU when n > 8
 
 template <int MaxN>
 struct ContribTable {
@@ -55,6 +57,18 @@ __device__ __forceinline__ void add8(float (&acc)[8], u32x4 x)
     acc[7] += bf16_hi(x.w);
 }
 
+__device__ __forceinline__ void set8(float (&acc)[8], u32x4 x)
+{
+    acc[0] = bf16_lo(x.x);
+    acc[1] = bf16_hi(x.x);
+    acc[2] = bf16_lo(x.y);
+    acc[3] = bf16_hi(x.y);
+    acc[4] = bf16_lo(x.z);
+    acc[5] = bf16_hi(x.z);
+    acc[6] = bf16_lo(x.w);
+    acc[7] = bf16_hi(x.w);
+}
+
 template <int MaxN>
 __device__ __forceinline__ uint16_t reduce_one(const ContribTable<MaxN> &c, int32_t n, int64_t j,
                                                const MeanDivisor &d)
@@ -77,36 +91,26 @@ __global__ __launch_bounds__(kBlock) void reduce_vec_kernel(ContribTable<MaxN> c
     u32x4 *o4 = reinterpret_cast<u32x4 *>(out + head);
     for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
         float acc[8];
-        {
-            u32x4 x = reinterpret_cast<const u32x4 *>(c.p[0] + head)[i];
-            acc[0] = bf16_lo(x.x);
-            acc[1] = bf16_hi(x.x);
-            acc[2] = bf16_lo(x.y);
-            acc[3] = bf16_hi(x.y);
-            acc[4] = bf16_lo(x.z);
-            acc[5] = bf16_hi(x.z);
-            acc[6] = bf16_lo(x.w);
-            acc[7] = bf16_hi(x.w);
+        for (int32_t k = 0; k < n; k += kLoadBatch) {
+            u32x4 x[kLoadBatch];
+#pragma unroll
+            for (int u = 0; u < kLoadBatch; ++u)
+                if (k + u < n)
+                    x[u] = load_stream(reinterpret_cast<const u32x4 *>(c.p[k + u] + head) + i);
+#pragma unroll
+            for (int u = 0; u < kLoadBatch; ++u) {
+                if (k + u == 0)
+                    set8(acc, x[u]);
+                else if (k + u < n)
+                    add8(acc, x[u]);
+            }
         }
-        int32_t k = 1;
-        for (; k + 4 <= n; k += 4) {
-            u32x4 x0 = reinterpret_cast<const u32x4 *>(c.p[k] + head)[i];
-            u32x4 x1 = reinterpret_cast<const u32x4 *>(c.p[k + 1] + head)[i];
-            u32x4 x2 = reinterpret_cast<const u32x4 *>(c.p[k + 2] + head)[i];
-            u32x4 x3 = reinterpret_cast<const u32x4 *>(c.p[k + 3] + head)[i];
-            add8(acc, x0);
-            add8(acc, x1);
-            add8(acc, x2);
-            add8(acc, x3);
-        }
-        for (; k < n; ++k)
-            add8(acc, reinterpret_cast<const u32x4 *>(c.p[k] + head)[i]);
         u32x4 r;
         r.x = pack_bf16x2(finish_mean(acc[0], d), finish_mean(acc[1], d));
         r.y = pack_bf16x2(finish_mean(acc[2], d), finish_mean(acc[3], d));
         r.z = pack_bf16x2(finish_mean(acc[4], d), finish_mean(acc[5], d));
         r.w = pack_bf16x2(finish_mean(acc[6], d), finish_mean(acc[7], d));
-        o4[i] = r;
+        store_stream(o4 + i, r);
     }
     if (blockIdx.x == 0) {
         int64_t tail_start = head + 8 * groups;
@@ -127,8 +131,6 @@ __global__ __launch_bounds__(kBlock) void reduce_scalar_kernel(ContribTable<MaxN
         out[j] = reduce_one(c, n, j, d);
 }
 
-int device_cu_count();
-
 template <int MaxN>
 static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t numel, uint16_t *out,
                                hipStream_t st, const MeanDivisor &d)
@@ -136,7 +138,6 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
     ContribTable<MaxN> c = {};
     for (int32_t k = 0; k < n; ++k)
         c.p[k] = static_cast<const uint16_t *>(contribs[k]);
-    const int64_t max_blocks = (int64_t)device_cu_count() * ZR_REDUCE_BLOCKS_PER_CU;
     int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(out) & 15)) & 15) / 2);
     if (head > numel)
         head = numel;
@@ -145,12 +146,12 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
         vec = aligned_to(c.p[k] + head, 16);
     if (vec) {
         int64_t groups = (numel - head) / 8;
-        int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((groups + kBlock - 1) / kBlock, max_blocks));
-        return launch(reduce_vec_kernel<MaxN>, dim3((unsigned)blocks), dim3(kBlock), st, c, n, out, numel, head,
-                      groups, d);
+        size_t lds = n > 8 ? kManyContribLds : 0;
+        return launch(reduce_vec_kernel<MaxN>, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock), lds, st, c, n,
+                      out, numel, head, groups, d);
     }
-    int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((numel + kBlock - 1) / kBlock, max_blocks));
-    return launch(reduce_scalar_kernel<MaxN>, dim3((unsigned)blocks), dim3(kBlock), st, c, n, out, numel, d);
+    return launch(reduce_scalar_kernel<MaxN>, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, c, n,
+                  out, numel, d);
 }
 
 }  // namespace zr

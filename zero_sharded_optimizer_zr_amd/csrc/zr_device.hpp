@@ -7,11 +7,27 @@
 
 namespace zr {
 
-// Native clang vectors: one 16-byte global access per lane (global_load/store_dwordx4).
+// Native clang vectors: one 16-byte (dwordx4) or 8-byte (dwordx2) global
+// access per lane.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;  // 4 wave64 per workgroup
+
+// Streaming accesses: every byte is touched once, so loads and stores carry the
+// non-temporal hint (the caches do not keep the line for reuse).
+template <typename T>
+__device__ __forceinline__ T load_stream(const T *p)
+{
+    return __builtin_nontemporal_load(p);
+}
+
+template <typename T>
+__device__ __forceinline__ void store_stream(T *p, T v)
+{
+    __builtin_nontemporal_store(v, p);
+}
 
 // bf16 -> fp32 is exact: the 16 bits are the upper half of the fp32 pattern.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -32,8 +48,11 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-// Global thread index and stride over a 1-D grid, 64-bit.
-__device__ __forceinline__ int64_t global_tid() { return (int64_t)blockIdx.x * blockDim.x + threadIdx.x; }
-__device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * blockDim.x; }
+// Global thread index and stride over a 1-D grid, 64-bit.  Every kernel is
+// launched with kBlock threads, so the block size is a compile-time constant:
+// reading blockDim.x would cost a vector load from the dispatch packet (and a
+// full memory wait) before each wave's first real load.
+__device__ __forceinline__ int64_t global_tid() { return (int64_t)blockIdx.x * kBlock + threadIdx.x; }
+__device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * kBlock; }
 
 }  // namespace zr

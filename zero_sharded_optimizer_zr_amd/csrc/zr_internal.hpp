@@ -32,6 +32,17 @@ void clear_error();
 void for_each_fragment(const zr_layout &L, int64_t begin, int64_t end,
                        const std::function<void(const zr_fragment &)> &fn);
 
+// Grid of `blocks` workgroups, clamped to what one launch dimension allows
+// (kernels loop over any remainder).
+inline dim3 grid_of(int64_t blocks)
+{
+    if (blocks < 1)
+        blocks = 1;
+    if (blocks > 0x7fffffff)
+        blocks = 0x7fffffff;
+    return dim3((unsigned)blocks);
+}
+
 inline bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 inline bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
@@ -42,9 +53,13 @@ inline bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbyte
 }
 
 // Launches `kernel` through hipLaunchKernel so the status of this launch is
-// returned directly (no sticky-error ambiguity).
+// returned directly (no sticky-error ambiguity).  `lds_bytes` of dynamic LDS is
+// reserved per workgroup; the streaming kernels never touch it and use it only
+// to cap how many workgroups a compute unit holds at once (160 KB of LDS per CU
+// on gfx950), which bounds the bytes in flight per HBM channel.
 template <typename... Params, typename... Args>
-zr_status launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream, Args &&...args)
+zr_status launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds_bytes, hipStream_t stream,
+                 Args &&...args)
 {
     std::tuple<Params...> values(std::forward<Args>(args)...);
     void *ptrs[sizeof...(Params) > 0 ? sizeof...(Params) : 1];
@@ -52,7 +67,7 @@ zr_status launch(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t s
         int i = 0;
         ((ptrs[i++] = static_cast<void *>(&v)), ...);
     }, values);
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, 0, stream);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, lds_bytes, stream);
     if (e != hipSuccess)
         return fail(ZR_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ZR_OK;
