@@ -71,7 +71,7 @@ def measured_traffic(per_launch_bytes):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs one GPU only (asked for --gpus {args.gpus}): this build shards nothing across GPUs",
+        print(f"bench.py runs one GPU only (asked for --gpus {args.gpus}): the library shards nothing across GPUs",
               file=sys.stderr)
         sys.exit(2)
 

@@ -1,7 +1,7 @@
 """Helpers for the GPU parity tests: device placement at chosen element
 offsets inside guarded allocations, bit views, and the parity tolerances.
 
-Tolerances (spec parity bar):
+Parity tolerances:
 * indexing, layout, pack/unpack, reduce: bit-exact;
 * fp32 master / m / v: |gpu - ref| <= 1e-6 |ref| + 1e-9;
 * bf16 parameter copy: within 1 bf16 ulp (order-mapped integers, +0 == -0).

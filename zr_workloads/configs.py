@@ -10,7 +10,7 @@ tensor lists stand in for the pages' example models:
 * the 1T-parameter model on 512 V100s of the DeepSpeed ZeRO-3 encyclopedia
   entry (baike.kuaisou.com), applications section.
 
-Shapes of the Llama-style and GPT-style lists are this build's reading of the
+Shapes of the Llama-style and GPT-style lists are a reading of the
 stated dimensions (the pages list no tensors).
 """
 from __future__ import annotations
