@@ -228,3 +228,46 @@ def test_flat_1t_nd512_shard_and_unpack():
     view = torch.empty(e - b, dtype=torch.bfloat16, device=dev)
     zr.zr_unpack(lay, out["param"], b, e, [(view, b)])
     assert torch.equal(view.view(torch.int16), out["param"].view(torch.int16))
+
+
+def test_single_calls_beyond_2_pow_31_elements():
+    """64-bit indexing: one AdamW, one reduce and one pack over more than 2^31
+    elements, at base offsets that need the head peel and the funnel path."""
+    dev = device()
+    n = (1 << 31) + 13
+    w = FLAT_7B
+    say("adamw / reduce over", n, "elements")
+    idx = sample_idx(n, 31, dev)
+    base = torch.empty(n + 8, dtype=torch.bfloat16, device=dev)
+    contribs = [base[3:3 + n], synth.normal_bf16(n + 8, 1e-3, 91, dev)[3:3 + n]]
+    contribs[0].copy_(synth.normal_bf16(n, 1e-3, 90, dev))
+    grad = torch.empty(n + 8, dtype=torch.bfloat16, device=dev)[3:3 + n]
+    zr.zr_reduce_slice(contribs, grad)
+    o_grad = oracle.reduce([take16(c, idx) for c in contribs])
+    assert_bits_equal(take16(grad, idx), o_grad, "reduce beyond 2^31")
+    del contribs, base
+    st = synth.shard_state(w, n, device=dev)
+    before = [take32(st[k], idx) for k in ("master", "exp_avg", "exp_avg_sq")]
+    param = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    zr.zr_adamw_step(grad, st["master"], st["exp_avg"], st["exp_avg_sq"], param, step=10, **w.hparams)
+    torch.cuda.synchronize()
+    o_param = np.zeros(idx.numel(), np.uint16)
+    oracle.adamw(o_grad, *before, o_param, step=10, **w.hparams)
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
+        assert_fp32_close(take32(st[k], idx), want, f"adamw beyond 2^31 {name}")
+    assert_bf16_within_1ulp(take16(param, idx), o_param, "adamw beyond 2^31 param")
+    del st, grad
+    torch.cuda.empty_cache()
+    # pack one tensor of n elements, shifted by 3 elements against the flat buffer
+    lay = zr.zr_layout_create([5, n], 1, 0)
+    src = torch.empty(n + 8, dtype=torch.int16, device=dev)[3:3 + n]
+    src.copy_(synth.random_bits16(n, 92, dev))
+    small = synth.random_bits16(5, 93, dev)
+    flat = torch.empty(n + 5, dtype=torch.int16, device=dev)
+    zr.zr_pack(lay, [small, src], flat, 0, n + 5)
+    assert torch.equal(flat[:5], small) and torch.equal(flat[5:], src)
+    back = torch.zeros(n, dtype=torch.int16, device=dev)
+    back_small = torch.zeros(5, dtype=torch.int16, device=dev)
+    zr.zr_unpack(lay, flat, 0, n + 5, [back_small, back])
+    assert torch.equal(back_small, small)
+    assert torch.equal(back, src)
