@@ -6,11 +6,12 @@
 // by HBM bandwidth at (2n + 2) bytes per element.  Each lane takes 8
 // consecutive elements (one 16-byte non-temporal load per contribution, one
 // 16-byte store), one group per lane over a grid that covers the slice;
-// contribution loads are issued eight at a time so several 16-byte reads are in
-// flight per lane.  With more than 8 contributions the kernel holds at most 2
-// workgroups per CU (LDS reserved, never touched): with n + 1 streams the DRAM
-// rows thrash when every CU is full (measured on MI355X at n = 64: 5.8 TB/s
-// uncapped, 6.4 TB/s capped).  The n device pointers travel by value in the
+// contribution loads are issued four at a time so several 16-byte reads are in
+// flight per lane.  With n + 1 concurrent streams the DRAM rows thrash when
+// every CU is full of waves, so the kernel caps its residency with LDS it
+// reserves and never touches: 4 workgroups per CU for 5..8 contributions, 2 for
+// more (measured on MI355X: n = 8 5.6 -> 6.0 TB/s, n = 64 5.8 -> 6.3 TB/s;
+// n <= 4 is best uncapped).  The n device pointers travel by value in the
 // kernel arguments.
 //
 // Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
@@ -26,8 +27,17 @@
 namespace zr {
 
 constexpr int kMaxContribs = 256;
-constexpr int kLoadBatch = 8;                  // contribution loads in flight per lane
-constexpr size_t kManyContribLds = 80 * 1024;  // 2 workgroups per CU when n > 8
+constexpr int kLoadBatch = 4;  // contribution loads in flight per lane
+
+// Dynamic LDS reserved per workgroup (160 KB per CU): residency cap by n.
+inline size_t residency_cap_lds(int32_t n)
+{
+    if (n > 8)
+        return 80 * 1024;  // 2 workgroups per CU
+    if (n > 4)
+        return 40 * 1024;  // 4 workgroups per CU
+    return 0;
+}
 
 template <int MaxN>
 struct ContribTable {
@@ -146,9 +156,8 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
         vec = aligned_to(c.p[k] + head, 16);
     if (vec) {
         int64_t groups = (numel - head) / 8;
-        size_t lds = n > 8 ? kManyContribLds : 0;
-        return launch(reduce_vec_kernel<MaxN>, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock), lds, st, c, n,
-                      out, numel, head, groups, d);
+        return launch(reduce_vec_kernel<MaxN>, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock),
+                      residency_cap_lds(n), st, c, n, out, numel, head, groups, d);
     }
     return launch(reduce_scalar_kernel<MaxN>, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, c, n,
                   out, numel, d);
