@@ -148,6 +148,34 @@ def main():
     elapsed = time.perf_counter() - start
     print(f"[bench] {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
 
+    # the same step with the gradient mean and AdamW fused into one pass
+    fused_events = {k: [] for k in ("pack", "reduce_adamw", "unpack")}
+
+    def fused_step(record):
+        def ev():
+            x = torch.cuda.Event(enable_timing=True)
+            x.record(stream)
+            return x
+        t0 = ev() if record else None
+        zr.zr_pack(lay, own_grad, contribs[0], b, e, stream=stream)
+        t1 = ev() if record else None
+        zr.zr_reduce_adamw_step(contribs, master, m, v, flat_param, step=t_step, stream=stream, **hp)
+        t2 = ev() if record else None
+        zr.zr_unpack(lay, flat_param, b, e, params, stream=stream)
+        if record:
+            t3 = ev()
+            for k, (x, y) in zip(fused_events, ((t0, t1), (t1, t2), (t2, t3))):
+                fused_events[k].append((x, y))
+
+    for _ in range(args.warmup):
+        fused_step(False)
+    torch.cuda.synchronize()
+    fstart = time.perf_counter()
+    for _ in range(args.steps):
+        fused_step(True)
+    torch.cuda.synchronize()
+    felapsed = time.perf_counter() - fstart
+
     for _ in range(args.copy_calibration):
         a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
         c = torch.empty_like(a)
@@ -168,6 +196,15 @@ def main():
     adamw_ms = kernels["adamw"]["ms_avg"]
     achieved = bytes_per["adamw"] / (adamw_ms * 1e-3) / 1e9
     traffic = measured_traffic(bytes_per["adamw"])
+
+    fbytes = {"pack": 4 * S, "reduce_adamw": (2 * n + 26) * S, "unpack": 4 * S}
+    fkernels = {}
+    for k in fused_events:
+        ms = [x.elapsed_time(y) for x, y in fused_events[k]]
+        avg = float(np.mean(ms))
+        fkernels[k] = {"ms_avg": round(avg, 4), "algorithmic_bytes": fbytes[k],
+                       "GBps": round(fbytes[k] / (avg * 1e-3) / 1e9, 1)}
+    fms = felapsed / args.steps * 1e3
 
     result = {
         "metric": METRIC,
@@ -191,6 +228,9 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": bytes_per["adamw"],
                      "bytes_per_element": 28},
         "kernels": kernels,
+        "fused_path": {"path": "pack+reduce_adamw+unpack", "ms_per_step": round(fms, 4),
+                       "value": S / (fms * 1e-3), "unit": "elements/s",
+                       "step_algorithmic_bytes": sum(fbytes.values()), "kernels": fkernels},
     }
 
     if not args.no_cpu_baseline:

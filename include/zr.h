@@ -10,6 +10,7 @@
  *   3. a fused mixed-precision AdamW step on the slice (zr_adamw_step)
  *   4. bit copies between per-tensor bf16 views and the flat buffer
  *                                                    (zr_pack / zr_unpack)
+ * and 2 + 3 in one pass (zr_reduce_adamw_step).
  *
  * Sources are web pages on DeepSpeed ZeRO-3, cited by title and section:
  *   [ENC]  "DeepSpeed ZeRO-3", encyclopedia entry (baike.kuaisou.com)
@@ -241,6 +242,30 @@ ZR_API zr_status zr_reduce_slice(const void *const *contribs, int32_t n, int64_t
  */
 ZR_API zr_status zr_adamw_step(const void *grad, float *master, float *exp_avg, float *exp_avg_sq,
                         void *param_out, int64_t numel, const zr_adamw_hparams *hp, void *stream);
+
+/* ------------------------------------------------- fused reduce + AdamW ---- */
+
+/*
+ * zr_reduce_slice followed by zr_adamw_step in one pass over the shard: the
+ * mean of the n bf16 gradient contributions is formed in fp32 (ascending k,
+ * one division by n), rounded to bf16, and used at once as the gradient of the
+ * AdamW update, without the bf16 gradient's round trip through memory.  Every
+ * output is bit for bit what the two calls in sequence produce.  After the
+ * ReduceScatter each rank updates its parameter shard with its gradient shard
+ * ([BLOG] "ZeRO-2: why gradients can be sharded too" and "ZeRO-1: why optimizer
+ * states can be sharded"; [CON] Stage 1 and Stage 2 mechanism).
+ *
+ * contribs: host array of n device pointers to bf16 [numel], 1 <= n <= 256.
+ * master, exp_avg, exp_avg_sq: device fp32 [numel], updated in place.
+ * param_out: device bf16 [numel] or NULL.  grad_out: device bf16 [numel] or
+ * NULL; when given it receives the bf16 mean (what zr_reduce_slice writes) and
+ * may be exactly contribs[0].  No other overlap between a contribution and an
+ * output, or between two outputs, is allowed.  hp as for zr_adamw_step.
+ * Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
+ */
+ZR_API zr_status zr_reduce_adamw_step(const void *const *contribs, int32_t n, float *master, float *exp_avg,
+                                      float *exp_avg_sq, void *param_out, void *grad_out, int64_t numel,
+                                      const zr_adamw_hparams *hp, void *stream);
 
 /* ------------------------------------------------------------- misc ------ */
 

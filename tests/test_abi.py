@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     lib = ctypes.CDLL(zr.LIBRARY)
     for name in names:
         assert hasattr(lib, name), name
@@ -258,3 +258,35 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         zr.zr_unpack(lay, torch.zeros(20, dtype=torch.int16)[::2], 0, 10, [torch.zeros(10, dtype=torch.int16)],
                      stream=0)
+
+
+@pytest.mark.parametrize("case,table,n,outs,numel,hp,code", [
+    ("null hp", "t2", 2, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, None, zr.ZR_EINVAL),
+    ("null table", None, 2, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, "hp", zr.ZR_EINVAL),
+    ("n = 0", "t2", 0, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, "hp", zr.ZR_EINVAL),
+    ("n = 257", "t2", 257, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, "hp", zr.ZR_EINVAL),
+    ("negative numel", "t2", 2, (A, A + 2**24, A + 2**25, A + 2**26, None), -1, "hp", zr.ZR_EINVAL),
+    ("null master", "t2", 2, (None, A + 2**24, A + 2**25, A + 2**26, None), 16, "hp", zr.ZR_EINVAL),
+    ("step 0", "t2", 2, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, _hp(step=0), zr.ZR_EINVAL),
+    ("odd param", "t2", 2, (A, A + 2**24, A + 2**25, A + 2**26 + 1, None), 16, "hp", zr.ZR_EALIGN),
+    ("m overlaps master", "t2", 2, (A, A + 32, A + 2**25, A + 2**26, None), 16, "hp", zr.ZR_EINVAL),
+    ("grad_out overlaps v", "t2", 2, (A, A + 2**24, A + 2**25, A + 2**26, A + 2**25 + 8), 16, "hp", zr.ZR_EINVAL),
+    ("contribution overlaps master", "tclash", 2, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, "hp",
+     zr.ZR_EINVAL),
+    ("grad_out inside contribs[1]", "t2", 2, (A, A + 2**24, A + 2**25, A + 2**26, A + 2**28 + 4), 16, "hp",
+     zr.ZR_EINVAL),
+    ("odd contribution", "todd", 2, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, "hp", zr.ZR_EALIGN),
+])
+def test_fused_validation(case, table, n, outs, numel, hp, code):
+    tables = {"t2": _table(A + 2**27, A + 2**28), "tclash": _table(A + 2**27, A + 8),
+              "todd": _table(A + 2**27, A + 2**28 + 1)}
+    hp = _hp() if hp == "hp" else hp
+    st = zr._lib.zr_reduce_adamw_step(tables.get(table), n, *outs[:4], outs[4], numel,
+                                      None if hp is None else ctypes.byref(hp), None)
+    assert st == code, (case, zr.zr_last_error())
+
+
+def test_fused_empty_is_a_no_op():
+    hp = _hp()
+    assert zr._lib.zr_reduce_adamw_step(_table(A, A + 64), 2, None, None, None, None, None, 0,
+                                        ctypes.byref(hp), None) == zr.ZR_OK

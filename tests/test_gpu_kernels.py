@@ -292,3 +292,71 @@ def test_gather_example_on_gpu(golden):
     w = torch.from_numpy(oracle.bf16_from_f32(np.array(gld["before"], np.float32)).view(np.int16)).to(device())
     zr.zr_unpack(lay, gathered, 0, 2, [w])
     assert list(oracle.f32_from_bf16(u16(w))) == gld["gathered"]
+
+
+# ------------------------------------------------------ fused reduce+AdamW ----
+
+def _fused_vs_separate(n, size, offsets, seed, with_param=True, with_grad=True, in_place=False, step=3,
+                       hp=HP):
+    """The fused call against zr_reduce_slice then zr_adamw_step on copies of the
+    same inputs: every output bit-identical; both within the oracle's bar."""
+    contribs = [_bits(synth.normal_bf16(size, 1e-3, seed + k)) for k in range(n)]
+    _, master, m, v = _adamw_inputs(size, seed + 100)
+    co, so = offsets
+    # separate path
+    pc = [Placed(c, co) for c in contribs]
+    grad = Placed(np.zeros(size, np.uint16), co)
+    zr.zr_reduce_slice([p.view for p in pc], grad.view)
+    pt, pm, pv = Placed(master, so), Placed(m, so), Placed(v, so)
+    pp = Placed(np.zeros(size, np.uint16), co) if with_param else None
+    zr.zr_adamw_step(grad.view, pt.view, pm.view, pv.view, pp.view if pp else None, step=step, **hp)
+    # fused path
+    fc = [Placed(c, co) for c in contribs]
+    ft, fm, fv = Placed(master, so), Placed(m, so), Placed(v, so)
+    fp = Placed(np.zeros(size, np.uint16), co) if with_param else None
+    if in_place:
+        fg = fc[0]
+    else:
+        fg = Placed(np.zeros(size, np.uint16), co) if with_grad else None
+    zr.zr_reduce_adamw_step([p.view for p in fc], ft.view, fm.view, fv.view, fp.view if fp else None,
+                            fg.view if fg else None, step=step, **hp)
+    torch.cuda.synchronize()
+    for p in fc + [ft, fm, fv, fp, fg]:
+        assert p is None or p.guards_intact()
+    for a, b, name in ((ft, pt, "master"), (fm, pm, "m"), (fv, pv, "v")):
+        assert_bits_equal(a.host(), b.host(), f"fused {name} n={n} size={size} offsets={offsets}")
+    if with_param:
+        assert_bits_equal(fp.host(), pp.host(), f"fused param n={n}")
+    if fg is not None:
+        assert_bits_equal(fg.host(), grad.host(), f"fused grad_out n={n}")
+    # and the composition of the oracle's two steps
+    o_grad = oracle.reduce(contribs)
+    ref = _adamw_ref(o_grad, master, m, v, step, with_param=with_param, hp=hp)
+    _check_adamw((ft.host(), fm.host(), fv.host(), fp.host() if fp else None), ref, f"fused vs oracle n={n}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 9, 64, 65])
+def test_fused_matches_separate_calls(n):
+    device()
+    say("fused n =", n)
+    _fused_vs_separate(n, 30_000 + 7 * n + 3, (0, 0), 300 + n)
+
+
+# (contribution / copy / mean offset, state offset) in elements: aligned; a head
+# peel that keeps every buffer vector-aligned ((1,1), (2,2), (3,3)); phases that
+# force the element-wise fallback ((1,0), (0,2), (2,1), (3,1))
+@pytest.mark.parametrize("size,offsets", [(0, (0, 0)), (1, (0, 0)), (3, (1, 1)), (4, (0, 0)), (5, (2, 1)),
+                                          (4099, (3, 3)), (4099, (1, 0)), (4099, (0, 2)), (65_537, (2, 2)),
+                                          (65_537, (3, 1))])
+def test_fused_sizes_and_paths(size, offsets):
+    device()
+    _fused_vs_separate(4, size, offsets, 7 + size)
+
+
+def test_fused_optional_outputs_and_in_place():
+    device()
+    _fused_vs_separate(4, 10_001, (0, 0), 11, with_param=False, with_grad=False)
+    _fused_vs_separate(8, 10_001, (0, 0), 12, with_param=True, with_grad=False)
+    _fused_vs_separate(8, 10_001, (0, 0), 13, with_param=False, with_grad=True)
+    _fused_vs_separate(4, 10_001, (2, 1), 14, in_place=True)
+    _fused_vs_separate(3, 10_001, (0, 0), 15, step=1000, hp=dict(HP, lr=1e-4, weight_decay=0.1))

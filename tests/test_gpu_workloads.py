@@ -271,3 +271,34 @@ def test_single_calls_beyond_2_pow_31_elements():
     zr.zr_unpack(lay, flat, 0, n + 5, [back_small, back])
     assert torch.equal(back_small, small)
     assert torch.equal(back, src)
+
+
+def test_fused_path_full_size_is_bit_identical():
+    """On the full 7e9 / N_d = 4 shard: the fused call and the two separate calls
+    give identical bits (a property at any size), and the fused outputs meet the
+    oracle's bar on the sampled elements."""
+    dev = device()
+    w = FLAT_7B
+    n = 1_750_000_000
+    idx = sample_idx(n, 77, dev)
+    contribs = synth.contributions(w, n, device=dev)
+    st = synth.shard_state(w, n, device=dev)
+    before = [take32(st[k], idx) for k in ("master", "exp_avg", "exp_avg_sq")]
+    fused = {k: v.clone() for k, v in st.items()}
+    fparam = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    zr.zr_reduce_adamw_step(contribs, fused["master"], fused["exp_avg"], fused["exp_avg_sq"], fparam,
+                            step=w.steps[0], **w.hparams)
+    grad = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    param = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    zr.zr_reduce_slice(contribs, grad)
+    zr.zr_adamw_step(grad, st["master"], st["exp_avg"], st["exp_avg_sq"], param, step=w.steps[0], **w.hparams)
+    torch.cuda.synchronize()
+    for k in ("master", "exp_avg", "exp_avg_sq"):
+        assert torch.equal(fused[k].view(torch.int32), st[k].view(torch.int32)), k
+    assert torch.equal(fparam.view(torch.int16), param.view(torch.int16))
+    o_grad = oracle.reduce([take16(c, idx) for c in contribs])
+    o_param = np.zeros(idx.numel(), np.uint16)
+    oracle.adamw(o_grad, *before, o_param, step=w.steps[0], **w.hparams)
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
+        assert_fp32_close(take32(fused[k], idx), want, f"fused {name}")
+    assert_bf16_within_1ulp(take16(fparam, idx), o_param, "fused param")

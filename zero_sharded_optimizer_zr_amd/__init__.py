@@ -20,7 +20,7 @@ import torch  # loads the process's HIP runtime before libzr binds to it
 __all__ = [
     "ZRError", "Layout", "zr_layout_create", "zr_layout_destroy", "zr_layout_query", "zr_layout_tensor",
     "zr_layout_rank_range", "zr_layout_fragments", "zr_layout_ledger_bytes", "zr_pack", "zr_unpack",
-    "zr_reduce_slice", "zr_adamw_step", "zr_last_error", "zr_abi_version", "LIBRARY",
+    "zr_reduce_slice", "zr_adamw_step", "zr_reduce_adamw_step", "zr_last_error", "zr_abi_version", "LIBRARY",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzr.so")
@@ -75,6 +75,7 @@ _SIGS = {
     "zr_unpack": ([_P, _P, _I64, _I64, _P, _I32, _P], _I32),
     "zr_reduce_slice": ([_P, _I32, _I64, _P, _P], _I32),
     "zr_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _P], _I32),
+    "zr_reduce_adamw_step": ([_P, _I32, _P, _P, _P, _P, _P, _I64, _P, _P], _I32),
     "zr_last_error": ([], ctypes.c_char_p),
     "zr_abi_version": ([], _I32),
 }
@@ -242,3 +243,20 @@ def zr_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tenso
     _check(_lib.zr_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                               _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
                               ctypes.byref(hp), _stream(stream)))
+
+
+def zr_reduce_adamw_step(contribs: Sequence[torch.Tensor], master: torch.Tensor, exp_avg: torch.Tensor,
+                         exp_avg_sq: torch.Tensor, param_out: Optional[torch.Tensor],
+                         grad_out: Optional[torch.Tensor] = None, *, lr: float, beta1: float, beta2: float,
+                         eps: float, weight_decay: float, step: int, grad_scale: float = 1.0,
+                         numel: Optional[int] = None, stream=None) -> None:
+    """zr_reduce_slice(contribs -> mean) then zr_adamw_step(mean, ...) in one pass;
+    grad_out (optional) receives the bf16 mean."""
+    n = len(contribs)
+    table = (ctypes.c_void_p * max(1, n))(*[_ptr(c, 2, f"contribs[{k}]") for k, c in enumerate(contribs)])
+    hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
+                  int(step))
+    numel = master.numel() if numel is None else int(numel)
+    _check(_lib.zr_reduce_adamw_step(table, n, _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                                     _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"),
+                                     _ptr(grad_out, 2, "grad_out"), numel, ctypes.byref(hp), _stream(stream)))

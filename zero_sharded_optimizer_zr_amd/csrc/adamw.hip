@@ -21,10 +21,7 @@
 //    is made from the updated fp32 master;
 //  - ZeRO tutorial (cnhsyj.com) 3.1: AdamW with lr, betas, eps, weight_decay.
 // The update is decoupled-weight-decay Adam (Loshchilov & Hutter, ICLR 2019).
-#include <cmath>
-
-#include "zr_device.hpp"
-#include "zr_internal.hpp"
+#include "zr_math.hpp"
 
 namespace zr {
 
@@ -32,28 +29,6 @@ namespace zr {
 #ifndef ZR_ADAMW_LDS_CAP
 #define ZR_ADAMW_LDS_CAP (32 * 1024)
 #endif
-
-struct AdamWScalars {
-    float beta1, one_minus_beta1;
-    float beta2, one_minus_beta2;
-    float decay;           // 1 - lr * weight_decay
-    float step_size;       // lr / (1 - beta1^t)
-    float inv_sqrt_bias2;  // 1 / sqrt(1 - beta2^t)
-    float eps;
-    float grad_scale;
-};
-
-// The one per-element update used by every code path (vector body, edges,
-// unaligned fallback), so all paths give the same bits.
-__device__ __forceinline__ void adamw_element(float graw, float &th, float &m, float &v, const AdamWScalars &s)
-{
-    float g = graw * s.grad_scale;
-    th = th * s.decay;
-    m = s.beta1 * m + s.one_minus_beta1 * g;
-    v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
-    float denom = __fsqrt_rn(v) * s.inv_sqrt_bias2 + s.eps;
-    th = th - s.step_size * __fdiv_rn(m, denom);
-}
 
 __device__ __forceinline__ void adamw_one(const uint16_t *grad, float *master, float *m, float *v,
                                           uint16_t *param, int64_t j, const AdamWScalars &s)
@@ -129,50 +104,26 @@ extern "C" zr_status zr_adamw_step(const void *grad, float *master, float *exp_a
                                    int64_t numel, const zr_adamw_hparams *hp, void *stream)
 {
     clear_error();
-    if (!hp)
-        return fail(ZR_EINVAL, "zr_adamw_step: hp is NULL");
+    zr_status st0 = check_adamw_hparams("zr_adamw_step", hp);
+    if (st0 != ZR_OK)
+        return st0;
     if (numel < 0)
         return fail(ZR_EINVAL, "zr_adamw_step: numel < 0");
     if (numel > 0 && (!grad || !master || !exp_avg || !exp_avg_sq))
         return fail(ZR_EINVAL, "zr_adamw_step: NULL buffer");
-    if (hp->step < 1)
-        return fail(ZR_EINVAL, "zr_adamw_step: step = %lld < 1", (long long)hp->step);
-    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
-        return fail(ZR_EINVAL, "zr_adamw_step: betas outside [0, 1)");
-    if (!(hp->eps > 0.0) || !std::isfinite(hp->eps))
-        return fail(ZR_EINVAL, "zr_adamw_step: eps must be finite and > 0");
-    if (!(hp->lr >= 0.0) || !std::isfinite(hp->lr) || !(hp->weight_decay >= 0.0) || !std::isfinite(hp->weight_decay))
-        return fail(ZR_EINVAL, "zr_adamw_step: lr and weight_decay must be finite and >= 0");
-    if (!std::isfinite(hp->grad_scale))
-        return fail(ZR_EINVAL, "zr_adamw_step: grad_scale must be finite");
     if (!aligned_to(grad, 2) || !aligned_to(param_out, 2) || !aligned_to(master, 4) || !aligned_to(exp_avg, 4) ||
         !aligned_to(exp_avg_sq, 4))
         return fail(ZR_EALIGN, "zr_adamw_step: buffers must be naturally aligned (bf16: 2 B, fp32: 4 B)");
     {
         const void *p[5] = {grad, master, exp_avg, exp_avg_sq, param_out};
         int64_t b[5] = {2 * numel, 4 * numel, 4 * numel, 4 * numel, param_out ? 2 * numel : 0};
-        for (int a = 0; a < 5; ++a)
-            for (int c = a + 1; c < 5; ++c)
-                if (p[a] && p[c] && overlaps(p[a], b[a], p[c], b[c]))
-                    return fail(ZR_EINVAL, "zr_adamw_step: buffers %d and %d overlap", a, c);
+        int x, y;
+        if (any_overlap(p, b, 5, &x, &y))
+            return fail(ZR_EINVAL, "zr_adamw_step: buffers %d and %d overlap", x, y);
     }
     if (numel == 0)
         return ZR_OK;
-
-    // per-step scalars in double, each rounded once to fp32
-    const double t = (double)hp->step;
-    const double bias1 = 1.0 - std::pow(hp->beta1, t);
-    const double bias2 = 1.0 - std::pow(hp->beta2, t);
-    AdamWScalars s;
-    s.beta1 = (float)hp->beta1;
-    s.one_minus_beta1 = (float)(1.0 - hp->beta1);
-    s.beta2 = (float)hp->beta2;
-    s.one_minus_beta2 = (float)(1.0 - hp->beta2);
-    s.decay = (float)(1.0 - hp->lr * hp->weight_decay);
-    s.step_size = (float)(hp->lr / bias1);
-    s.inv_sqrt_bias2 = (float)(1.0 / std::sqrt(bias2));
-    s.eps = (float)hp->eps;
-    s.grad_scale = (float)hp->grad_scale;
+    const AdamWScalars s = adamw_scalars(*hp);
 
     auto g = static_cast<const uint16_t *>(grad);
     auto p = static_cast<uint16_t *>(param_out);

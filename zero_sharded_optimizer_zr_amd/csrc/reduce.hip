@@ -19,14 +19,10 @@
 // leaves rank r with slice r of the averaged gradient: [2,6] and [4,10] give
 // [3] and [8]) and its ledger section (bf16 gradients); ZeRO-1/2/3 concept page
 // (compassingai.com), Stage 2 and Stage 3 mechanism.
-#include <algorithm>
-
-#include "zr_device.hpp"
-#include "zr_internal.hpp"
+#include "zr_math.hpp"
 
 namespace zr {
 
-constexpr int kMaxContribs = 256;
 constexpr int kLoadBatch = 4;  // contribution loads in flight per lane
 
 // Dynamic LDS reserved per workgroup (160 KB per CU): residency cap by n.
@@ -37,22 +33,6 @@ inline size_t residency_cap_lds(int32_t n)
     if (n > 4)
         return 40 * 1024;  // 4 workgroups per CU
     return 0;
-}
-
-template <int MaxN>
-struct ContribTable {
-    const uint16_t *p[MaxN];
-};
-
-struct MeanDivisor {
-    float n;      // (float)n
-    float inv;    // 1/n, exact when n is a power of two
-    int32_t pow2; // multiply by inv (same bits as dividing by n) instead of dividing
-};
-
-__device__ __forceinline__ float finish_mean(float sum, const MeanDivisor &d)
-{
-    return d.pow2 ? sum * d.inv : __fdiv_rn(sum, d.n);
 }
 
 __device__ __forceinline__ void add8(float (&acc)[8], u32x4 x)
@@ -77,16 +57,6 @@ __device__ __forceinline__ void set8(float (&acc)[8], u32x4 x)
     acc[5] = bf16_hi(x.z);
     acc[6] = bf16_lo(x.w);
     acc[7] = bf16_hi(x.w);
-}
-
-template <int MaxN>
-__device__ __forceinline__ uint16_t reduce_one(const ContribTable<MaxN> &c, int32_t n, int64_t j,
-                                               const MeanDivisor &d)
-{
-    float sum = bf16_to_f32(c.p[0][j]);
-    for (int32_t k = 1; k < n; ++k)
-        sum += bf16_to_f32(c.p[k][j]);
-    return (uint16_t)f32_to_bf16(finish_mean(sum, d));
 }
 
 // Vector body over `groups` groups of 8 elements from element `head` (where
@@ -192,10 +162,7 @@ extern "C" zr_status zr_reduce_slice(const void *const *contribs, int32_t n, int
     if (numel == 0)
         return ZR_OK;
 
-    MeanDivisor d;
-    d.n = (float)n;
-    d.inv = 1.0f / (float)n;
-    d.pow2 = (n & (n - 1)) == 0;
+    const MeanDivisor d = mean_divisor(n);
     auto o = static_cast<uint16_t *>(out);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (n <= 8)
