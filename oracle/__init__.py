@@ -51,6 +51,16 @@ def _load():
         lib.zr_oracle_reduce.restype = None
         lib.zr_oracle_adamw.argtypes = [p, p, p, p, p, i64, d, d, d, d, d, d, i64]
         lib.zr_oracle_adamw.restype = None
+        lib.zr_oracle_f16_from_f32.argtypes = [p, i64, p]
+        lib.zr_oracle_f16_from_f32.restype = None
+        lib.zr_oracle_f32_from_f16.argtypes = [p, i64, p]
+        lib.zr_oracle_f32_from_f16.restype = None
+        lib.zr_oracle_reduce_f16.argtypes = [p, i32, i64, p]
+        lib.zr_oracle_reduce_f16.restype = None
+        lib.zr_oracle_found_inf_f16.argtypes = [p, i64]
+        lib.zr_oracle_found_inf_f16.restype = i32
+        lib.zr_oracle_adamw_f16.argtypes = [p, p, p, p, p, i64, d, d, d, d, d, d, i64, d]
+        lib.zr_oracle_adamw_f16.restype = None
         _lib = lib
     return _lib
 
@@ -145,6 +155,116 @@ def adamw(grad: np.ndarray, master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq:
     _load().zr_oracle_adamw(_ptr(grad), _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), pp, n,
                             float(lr), float(beta1), float(beta2), float(eps),
                             float(weight_decay), float(grad_scale), int(step))
+
+
+# ------------------------------------------------------------------ fp16 ----
+#
+# fp16 parameters and gradients with dynamic loss scaling: the ZeRO tutorial
+# (cnhsyj.com) 3.1 sets fp16 with a dynamic loss scale (loss_scale 0), window
+# 1000 and initial scale 2^16, and 4.2 recommends dynamic scaling for fp16
+# gradients that are very small or very large; the concept page
+# (compassingai.com) 16 B/param table uses fp16 parameters and gradients.
+
+def f16_from_f32(x: np.ndarray) -> np.ndarray:
+    """fp32 -> fp16 bits, round to nearest even; overflow to inf; NaN to the
+    quiet NaN 0x7e00 with the input's sign."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().zr_oracle_f16_from_f32(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def f32_from_f16(h: np.ndarray) -> np.ndarray:
+    """fp16 bits -> fp32 (exact)."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    _load().zr_oracle_f32_from_f16(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+def reduce_f16(contribs: Sequence[np.ndarray], out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Mean of n fp16 contributions (fp32 sum in ascending k, one division, fp16)."""
+    numel = contribs[0].size
+    for k, c in enumerate(contribs):
+        _check(c, np.uint16, f"contribs[{k}]")
+        if c.size != numel:
+            raise ValueError("contributions differ in length")
+    if out is None:
+        out = np.empty(numel, dtype=np.uint16)
+    table = (ctypes.c_void_p * len(contribs))(*[_ptr(c) for c in contribs])
+    _load().zr_oracle_reduce_f16(ctypes.cast(table, ctypes.c_void_p), len(contribs), numel, _ptr(out))
+    return out
+
+
+def found_inf_f16(x: np.ndarray) -> bool:
+    """True if any fp16 value is inf or NaN."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    return bool(_load().zr_oracle_found_inf_f16(_ptr(x), x.size))
+
+
+def adamw_f16(grad: np.ndarray, master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
+              param_out: Optional[np.ndarray], *, lr: float, beta1: float, beta2: float, eps: float,
+              weight_decay: float, step: int, loss_scale: float, grad_scale: float = 1.0) -> None:
+    """The AdamW step of ``adamw`` on an fp16 gradient that carries the loss
+    scale (divided out before the update), with an fp16 copy."""
+    n = grad.size
+    _check(grad, np.uint16, "grad")
+    for name, a in (("master", master), ("exp_avg", exp_avg), ("exp_avg_sq", exp_avg_sq)):
+        _check(a, np.float32, name)
+        if a.size != n:
+            raise ValueError(f"{name} has the wrong length")
+    pp = None
+    if param_out is not None:
+        _check(param_out, np.uint16, "param_out")
+        pp = _ptr(param_out)
+    _load().zr_oracle_adamw_f16(_ptr(grad), _ptr(master), _ptr(exp_avg), _ptr(exp_avg_sq), pp, n,
+                                float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                                float(grad_scale), int(step), float(loss_scale))
+
+
+class LossScale:
+    """Dynamic loss scale, the plain rule: a step whose gradient holds an inf or
+    NaN is skipped and the scale is divided by ``factor`` (not below
+    ``min_scale``); after ``window`` consecutive clean steps the scale is
+    multiplied by ``factor``.  Defaults follow the tutorial's fp16 config
+    (initial scale 2^16, window 1000); the factor 2 and the floor 1 are the
+    customary values the page leaves implicit."""
+
+    def __init__(self, initial: float = 2.0 ** 16, window: int = 1000, factor: float = 2.0,
+                 min_scale: float = 1.0):
+        self.scale = float(initial)
+        self.window = int(window)
+        self.factor = float(factor)
+        self.min_scale = float(min_scale)
+        self.good_steps = 0
+        self.skipped = 0
+
+    def update(self, found_inf: bool) -> None:
+        if found_inf:
+            self.scale = max(self.scale / self.factor, self.min_scale)
+            self.good_steps = 0
+            self.skipped += 1
+        else:
+            self.good_steps += 1
+            if self.good_steps == self.window:
+                self.scale = self.scale * self.factor
+                self.good_steps = 0
+
+
+def step_f16(contribs: Sequence[np.ndarray], master: np.ndarray, exp_avg: np.ndarray, exp_avg_sq: np.ndarray,
+             param_out: Optional[np.ndarray], scaler: LossScale, *, lr: float, beta1: float, beta2: float,
+             eps: float, weight_decay: float, step: int, grad_scale: float = 1.0) -> np.ndarray:
+    """One fp16 step with dynamic loss scaling: the mean of the scaled fp16
+    contributions; if it holds an inf or NaN the update is skipped (state and
+    copy untouched), else AdamW on the unscaled mean; then the scale update.
+    Returns the fp16 mean."""
+    grad = reduce_f16(contribs)
+    inf = found_inf_f16(grad)
+    if not inf:
+        adamw_f16(grad, master, exp_avg, exp_avg_sq, param_out, lr=lr, beta1=beta1, beta2=beta2, eps=eps,
+                  weight_decay=weight_decay, step=step, loss_scale=scaler.scale, grad_scale=grad_scale)
+    scaler.update(inf)
+    return grad
 
 
 # ---------------------------------------------------------------- layout ----

@@ -147,3 +147,134 @@ void zr_oracle_adamw(const uint16_t *grad, float *master, float *exp_avg, float 
             param_out[i] = f32_to_bf16(master[i]);
     }
 }
+
+/* ---------------------------------------------------------------- fp16 ---- */
+
+/*
+ * fp16 variant of the step (fp16 parameters and gradients with dynamic loss
+ * scaling): the ZeRO tutorial (cnhsyj.com) 3.1 configures fp16 with a dynamic
+ * loss scale (window 1000, initial scale 2^16) and 4.2 recommends dynamic
+ * scaling for fp16 gradients that are very small or very large; the ZeRO-1/2/3
+ * concept page (compassingai.com), 16 B/param table and Stage 1 mechanism, uses
+ * fp16 parameters and gradients and a 16-bit copy of the fp32 master.
+ */
+
+/* fp16 -> fp32, exact. */
+static float f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    uint32_t exp = (h >> 10) & 0x1fu;
+    uint32_t man = h & 0x3ffu;
+    float f;
+    if (exp == 0x1fu) {                     /* inf or NaN */
+        uint32_t u = sign | 0x7f800000u | (man << 13);
+        memcpy(&f, &u, sizeof f);
+        return f;
+    }
+    if (exp == 0) {                         /* zero or subnormal: man * 2^-24 */
+        f = (float)man * 5.9604644775390625e-08f;
+        return sign ? -f : f;
+    }
+    uint32_t u = sign | ((exp + 112u) << 23) | (man << 13);
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* fp32 -> fp16, round to nearest, ties to even; overflow -> inf; NaN -> the
+ * quiet NaN 0x7e00 with the input's sign. */
+static uint16_t f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+    float a = fabsf(f);
+    if (a != a)
+        return (uint16_t)(sign | 0x7e00u);
+    if (a >= 65520.0f)                      /* 65504 + half an ulp rounds up to inf */
+        return (uint16_t)(sign | 0x7c00u);
+    if (a < 6.103515625e-05f) {             /* below 2^-14: subnormal result, unit 2^-24 */
+        double q = (double)a * 16777216.0;  /* exact: a is a float, 2^24 scaling */
+        double r = floor(q);
+        double rem = q - r;
+        uint32_t m = (uint32_t)r;
+        if (rem > 0.5 || (rem == 0.5 && (m & 1u)))
+            m += 1u;                        /* may carry into the smallest normal, 0x0400 */
+        return (uint16_t)(sign | m);
+    }
+    /* normal: keep 10 fraction bits of the fp32 significand, RNE on the 13 dropped */
+    uint32_t au = u & 0x7fffffffu;
+    uint32_t exp = (au >> 23) - 112u;       /* rebias 127 -> 15 */
+    uint32_t man = (au >> 13) & 0x3ffu;
+    uint32_t dropped = au & 0x1fffu;
+    uint32_t h = (exp << 10) | man;
+    if (dropped > 0x1000u || (dropped == 0x1000u && (man & 1u)))
+        h += 1u;                            /* carries into the exponent correctly */
+    return (uint16_t)(sign | h);
+}
+
+void zr_oracle_f16_from_f32(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f32_to_f16(x[i]);
+}
+
+void zr_oracle_f32_from_f16(const uint16_t *x, int64_t n, float *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f16_to_f32(x[i]);
+}
+
+/* Mean of n fp16 contributions: fp32 sum in ascending k, one division, fp16. */
+void zr_oracle_reduce_f16(const uint16_t *const *contribs, int32_t n, int64_t numel, uint16_t *out)
+{
+    for (int64_t i = 0; i < numel; ++i) {
+        float sum = f16_to_f32(contribs[0][i]);
+        for (int32_t k = 1; k < n; ++k)
+            sum = sum + f16_to_f32(contribs[k][i]);
+        out[i] = f32_to_f16(sum / (float)n);
+    }
+}
+
+/* 1 if any fp16 value is inf or NaN. */
+int32_t zr_oracle_found_inf_f16(const uint16_t *x, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        if ((x[i] & 0x7c00u) == 0x7c00u)
+            return 1;
+    return 0;
+}
+
+/*
+ * AdamW step on an fp16 gradient scaled by the loss scale: the gradient is
+ * divided by the scale (multiplied by 1/scale) before the update, and the
+ * 16-bit copy is fp16.  Otherwise the same update as zr_oracle_adamw, in
+ * double, stored in fp32.  The caller skips the call for a step whose
+ * gradient overflowed.
+ */
+void zr_oracle_adamw_f16(const uint16_t *grad, float *master, float *exp_avg, float *exp_avg_sq,
+                         uint16_t *param_out, int64_t numel,
+                         double lr, double beta1, double beta2, double eps,
+                         double weight_decay, double grad_scale, int64_t step, double loss_scale)
+{
+    double bias1 = 1.0 - pow(beta1, (double)step);
+    double bias2 = 1.0 - pow(beta2, (double)step);
+    double decay = 1.0 - lr * weight_decay;
+    double unscale = 1.0 / loss_scale;
+    for (int64_t i = 0; i < numel; ++i) {
+        double g = (double)f16_to_f32(grad[i]) * unscale * grad_scale;
+        double th = (double)master[i];
+        double m = (double)exp_avg[i];
+        double v = (double)exp_avg_sq[i];
+
+        th = th * decay;
+        m = beta1 * m + (1.0 - beta1) * g;
+        v = beta2 * v + (1.0 - beta2) * g * g;
+        th = th - lr * (m / bias1) / (sqrt(v / bias2) + eps);
+
+        master[i] = (float)th;
+        exp_avg[i] = (float)m;
+        exp_avg_sq[i] = (float)v;
+        if (param_out)
+            param_out[i] = f32_to_f16(master[i]);
+    }
+}
