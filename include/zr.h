@@ -10,7 +10,8 @@
  *   3. a fused mixed-precision AdamW step on the slice (zr_adamw_step)
  *   4. bit copies between per-tensor bf16 views and the flat buffer
  *                                                    (zr_pack / zr_unpack)
- * and 2 + 3 in one pass (zr_reduce_adamw_step).
+ * and 2 + 3 in one pass (zr_reduce_adamw_step), and an fp16 variant of 2 + 3
+ * with dynamic loss scaling (zr_*_f16, zr_loss_scale_*).
  *
  * Sources are web pages on DeepSpeed ZeRO-3, cited by title and section:
  *   [ENC]  "DeepSpeed ZeRO-3", encyclopedia entry (baike.kuaisou.com)
@@ -266,6 +267,66 @@ ZR_API zr_status zr_adamw_step(const void *grad, float *master, float *exp_avg, 
 ZR_API zr_status zr_reduce_adamw_step(const void *const *contribs, int32_t n, float *master, float *exp_avg,
                                       float *exp_avg_sq, void *param_out, void *grad_out, int64_t numel,
                                       const zr_adamw_hparams *hp, void *stream);
+
+/* ------------------------------------------------- fp16 + loss scaling ---- */
+
+/*
+ * fp16 variant of the step with dynamic loss scaling.  The backward pass gives
+ * fp16 gradients multiplied by the loss scale S.  Per step:
+ *   zr_reduce_slice_f16   mean of the n fp16 contributions (fp32 sum, one
+ *                         division, fp16 round to nearest even); sets
+ *                         ls->found_inf if any mean is inf or NaN;
+ *   zr_adamw_step_f16     when ls->found_inf is clear: AdamW on g / S with an
+ *                         fp16 copy; when it is set: nothing is written (the
+ *                         step is skipped);
+ *   zr_loss_scale_update  on overflow S <- max(S / factor, min_scale) and the
+ *                         clean-step count restarts; otherwise after `window`
+ *                         consecutive clean steps S <- S * factor; then
+ *                         ls->found_inf is cleared.
+ * [TUT] 3.1 (fp16 with a dynamic loss scale, window 1000, initial scale 2^16)
+ * and 4.2 (dynamic scaling for fp16 gradients that are very small or very
+ * large); [CON] 16 B/param table (fp16 parameters and gradients) and Stage 1
+ * mechanism (16-bit copy of the updated fp32 master).  The skip-and-rescale
+ * rule is standard dynamic loss scaling (Micikevicius et al., ICLR 2018).
+ * fp16 NaN results are the quiet NaN sign | 0x7e00.
+ *
+ * The record lives in device memory (caller-allocated, 4-byte aligned) and is
+ * only read and written by the kernels, in stream order; the host never has to
+ * synchronise to run a step.
+ */
+typedef struct zr_loss_scale {
+    float   scale;       /* current loss scale S */
+    int32_t good_steps;  /* consecutive clean steps since the last change */
+    int32_t found_inf;   /* set by the overflow checks, cleared by zr_loss_scale_update */
+    int32_t skipped;     /* steps skipped so far */
+} zr_loss_scale;
+
+/* Device record <- {initial_scale, 0, 0, 0}.  initial_scale finite and > 0.
+ * Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP. */
+ZR_API zr_status zr_loss_scale_init(zr_loss_scale *ls, float initial_scale, void *stream);
+
+/* Mean of n fp16 contributions into out (fp16 [numel]); ls may be NULL (no
+ * overflow flag).  Same buffer rules as zr_reduce_slice; ls must not overlap
+ * a buffer.  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP. */
+ZR_API zr_status zr_reduce_slice_f16(const void *const *contribs, int32_t n, int64_t numel, void *out,
+                                     zr_loss_scale *ls, void *stream);
+
+/* Sets ls->found_inf if any of grad (fp16 [numel]) is inf or NaN (for
+ * gradients reduced by other means).  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP. */
+ZR_API zr_status zr_check_finite_f16(const void *grad, int64_t numel, zr_loss_scale *ls, void *stream);
+
+/* AdamW on the fp16 gradient divided by ls->scale (then times hp->grad_scale),
+ * fp16 copy into param_out (or NULL); skipped entirely while ls->found_inf is
+ * set.  Same buffer rules as zr_adamw_step.
+ * Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP. */
+ZR_API zr_status zr_adamw_step_f16(const void *grad, float *master, float *exp_avg, float *exp_avg_sq,
+                                   void *param_out, int64_t numel, const zr_adamw_hparams *hp,
+                                   const zr_loss_scale *ls, void *stream);
+
+/* The scale rule above (one device thread).  window >= 1, factor finite and
+ * > 1, min_scale finite and > 0.  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP. */
+ZR_API zr_status zr_loss_scale_update(zr_loss_scale *ls, int32_t window, float factor, float min_scale,
+                                      void *stream);
 
 /* ------------------------------------------------------------- misc ------ */
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 19
     lib = ctypes.CDLL(zr.LIBRARY)
     for name in names:
         assert hasattr(lib, name), name
@@ -290,3 +290,40 @@ def test_fused_empty_is_a_no_op():
     hp = _hp()
     assert zr._lib.zr_reduce_adamw_step(_table(A, A + 64), 2, None, None, None, None, None, 0,
                                         ctypes.byref(hp), None) == zr.ZR_OK
+
+
+def test_fp16_validation():
+    L = zr._lib
+    hp = _hp()
+    ls = A + 2**30
+    # loss-scale record
+    assert L.zr_loss_scale_init(None, 65536.0, None) == zr.ZR_EINVAL
+    assert L.zr_loss_scale_init(ls + 2, 65536.0, None) == zr.ZR_EALIGN
+    assert L.zr_loss_scale_init(ls, 0.0, None) == zr.ZR_EINVAL
+    assert L.zr_loss_scale_init(ls, float("inf"), None) == zr.ZR_EINVAL
+    assert L.zr_loss_scale_update(ls, 0, 2.0, 1.0, None) == zr.ZR_EINVAL
+    assert L.zr_loss_scale_update(ls, 1000, 1.0, 1.0, None) == zr.ZR_EINVAL
+    assert L.zr_loss_scale_update(ls, 1000, 2.0, 0.0, None) == zr.ZR_EINVAL
+    assert L.zr_loss_scale_update(None, 1000, 2.0, 1.0, None) == zr.ZR_EINVAL
+    # finite check
+    assert L.zr_check_finite_f16(A, 16, None, None) == zr.ZR_EINVAL
+    assert L.zr_check_finite_f16(A + 1, 16, ls, None) == zr.ZR_EALIGN
+    assert L.zr_check_finite_f16(ls - 8, 16, ls, None) == zr.ZR_EINVAL     # record inside grad
+    assert L.zr_check_finite_f16(A, -1, ls, None) == zr.ZR_EINVAL
+    assert L.zr_check_finite_f16(None, 0, ls, None) == zr.ZR_OK
+    # fp16 mean
+    t = _table(A + 2**21, A + 2**20)
+    assert L.zr_reduce_slice_f16(t, 0, 16, A, None, None) == zr.ZR_EINVAL
+    assert L.zr_reduce_slice_f16(t, 2, 16, A + 1, None, None) == zr.ZR_EALIGN
+    assert L.zr_reduce_slice_f16(t, 2, 16, A, ls + 1, None) == zr.ZR_EALIGN
+    assert L.zr_reduce_slice_f16(t, 2, 16, A + 2**20 + 4, None, None) == zr.ZR_EINVAL
+    assert L.zr_reduce_slice_f16(t, 2, 16, A, A + 2**21 + 8, None) == zr.ZR_EINVAL   # record inside a contribution
+    assert L.zr_reduce_slice_f16(t, 2, 0, A, None, None) == zr.ZR_OK
+    # loss-scaled AdamW
+    args = (A, A + 2**22, A + 2**23, A + 2**24, A + 2**25)
+    assert L.zr_adamw_step_f16(*args, 16, ctypes.byref(hp), None, None) == zr.ZR_EINVAL
+    assert L.zr_adamw_step_f16(*args, 16, None, ls, None) == zr.ZR_EINVAL
+    assert L.zr_adamw_step_f16(*args, 16, ctypes.byref(_hp(step=0)), ls, None) == zr.ZR_EINVAL
+    assert L.zr_adamw_step_f16(A, A + 2**22 + 2, *args[2:], 16, ctypes.byref(hp), ls, None) == zr.ZR_EALIGN
+    assert L.zr_adamw_step_f16(*args, 16, ctypes.byref(hp), A + 2**23 + 16, None) == zr.ZR_EINVAL  # record in m
+    assert L.zr_adamw_step_f16(*args, 0, ctypes.byref(hp), ls, None) == zr.ZR_OK

@@ -302,3 +302,48 @@ def test_fused_path_full_size_is_bit_identical():
     for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
         assert_fp32_close(take32(fused[k], idx), want, f"fused {name}")
     assert_bf16_within_1ulp(take16(fparam, idx), o_param, "fused param")
+
+
+def test_fp16_loss_scaled_step_full_size():
+    """fp16 path on the 1.75e9-element shard with loss scale 2^16: a clean step
+    meets the oracle's bar on the samples; a step whose gradient holds one inf
+    leaves every state byte unchanged and halves the scale."""
+    dev = device()
+    n = 1_750_000_000
+    w = FLAT_7B
+    idx = sample_idx(n, 161, dev)
+    contribs = [(synth.normal_f32(n, 1e-3 * 65536.0, 900 + k, dev)).to(torch.float16) for k in range(4)]
+    st = synth.shard_state(w, n, device=dev)
+    before = [take32(st[k], idx) for k in ("master", "exp_avg", "exp_avg_sq")]
+    ls = zr.loss_scale_record(dev)
+    zr.zr_loss_scale_init(ls, 65536.0)
+    grad = torch.empty(n, dtype=torch.float16, device=dev)
+    param = torch.empty(n, dtype=torch.float16, device=dev)
+    zr.zr_reduce_slice_f16(contribs, grad, ls)
+    zr.zr_adamw_step_f16(grad, st["master"], st["exp_avg"], st["exp_avg_sq"], param, ls, step=10, **w.hparams)
+    zr.zr_loss_scale_update(ls)
+    torch.cuda.synchronize()
+    o_grad = oracle.reduce_f16([take16(c, idx) for c in contribs])
+    assert_bits_equal(take16(grad, idx), o_grad, "fp16 mean")
+    o_param = np.zeros(idx.numel(), np.uint16)
+    oracle.adamw_f16(o_grad, *before, o_param, step=10, loss_scale=65536.0, **w.hparams)
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
+        assert_fp32_close(take32(st[k], idx), want, f"fp16 step {name}")
+    d = np.abs(oracle.f32_from_f16(take16(param, idx)).astype(np.float64) -
+               oracle.f32_from_f16(o_param).astype(np.float64))
+    assert np.all(d <= np.abs(oracle.f32_from_f16(o_param)) * 2.0 ** -10 + 2.0 ** -24)   # within 1 fp16 ulp
+    r = ls.cpu()
+    assert float(r.view(torch.float32)[0]) == 65536.0 and int(r[1]) == 1 and int(r[2]) == 0
+    # second step: one overflowed value in one contribution -> skipped
+    contribs[3].view(torch.int16)[n // 3] = 0x7C00
+    snap = {k: v.clone() for k, v in st.items()}
+    psnap = param.clone()
+    zr.zr_reduce_slice_f16(contribs, grad, ls)
+    zr.zr_adamw_step_f16(grad, st["master"], st["exp_avg"], st["exp_avg_sq"], param, ls, step=11, **w.hparams)
+    zr.zr_loss_scale_update(ls)
+    torch.cuda.synchronize()
+    for k in snap:
+        assert torch.equal(snap[k].view(torch.int32), st[k].view(torch.int32)), k
+    assert torch.equal(psnap.view(torch.int16), param.view(torch.int16))
+    r = ls.cpu()
+    assert float(r.view(torch.float32)[0]) == 32768.0 and int(r[3]) == 1

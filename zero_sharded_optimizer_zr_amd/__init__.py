@@ -20,7 +20,9 @@ import torch  # loads the process's HIP runtime before libzr binds to it
 __all__ = [
     "ZRError", "Layout", "zr_layout_create", "zr_layout_destroy", "zr_layout_query", "zr_layout_tensor",
     "zr_layout_rank_range", "zr_layout_fragments", "zr_layout_ledger_bytes", "zr_pack", "zr_unpack",
-    "zr_reduce_slice", "zr_adamw_step", "zr_reduce_adamw_step", "zr_last_error", "zr_abi_version", "LIBRARY",
+    "zr_reduce_slice", "zr_adamw_step", "zr_reduce_adamw_step", "zr_loss_scale_init", "zr_reduce_slice_f16",
+    "zr_check_finite_f16", "zr_adamw_step_f16", "zr_loss_scale_update", "loss_scale_record", "zr_last_error",
+    "zr_abi_version", "LIBRARY",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzr.so")
@@ -76,6 +78,11 @@ _SIGS = {
     "zr_reduce_slice": ([_P, _I32, _I64, _P, _P], _I32),
     "zr_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _P], _I32),
     "zr_reduce_adamw_step": ([_P, _I32, _P, _P, _P, _P, _P, _I64, _P, _P], _I32),
+    "zr_loss_scale_init": ([_P, ctypes.c_float, _P], _I32),
+    "zr_reduce_slice_f16": ([_P, _I32, _I64, _P, _P, _P], _I32),
+    "zr_check_finite_f16": ([_P, _I64, _P, _P], _I32),
+    "zr_adamw_step_f16": ([_P, _P, _P, _P, _P, _I64, _P, _P, _P], _I32),
+    "zr_loss_scale_update": ([_P, _I32, ctypes.c_float, ctypes.c_float, _P], _I32),
     "zr_last_error": ([], ctypes.c_char_p),
     "zr_abi_version": ([], _I32),
 }
@@ -260,3 +267,57 @@ def zr_reduce_adamw_step(contribs: Sequence[torch.Tensor], master: torch.Tensor,
     _check(_lib.zr_reduce_adamw_step(table, n, _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                                      _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"),
                                      _ptr(grad_out, 2, "grad_out"), numel, ctypes.byref(hp), _stream(stream)))
+
+
+# ------------------------------------------------------ fp16 + loss scale ----
+
+def loss_scale_record(device=None) -> torch.Tensor:
+    """A device tensor holding one zr_loss_scale record (16 bytes: float scale,
+    int32 good_steps, int32 found_inf, int32 skipped), uninitialised."""
+    return torch.empty(4, dtype=torch.int32, device=device if device is not None else "cuda")
+
+
+def _ls(ls: Optional[torch.Tensor]) -> Optional[int]:
+    if ls is None:
+        return None
+    p = _ptr(ls, 4, "ls")
+    if ls.numel() < 4:
+        raise ValueError("ls must hold at least 16 bytes")
+    return p
+
+
+def zr_loss_scale_init(ls: torch.Tensor, initial_scale: float = 2.0 ** 16, stream=None) -> None:
+    _check(_lib.zr_loss_scale_init(_ls(ls), float(initial_scale), _stream(stream)))
+
+
+def zr_reduce_slice_f16(contribs: Sequence[torch.Tensor], out: torch.Tensor, ls: Optional[torch.Tensor] = None,
+                        numel: Optional[int] = None, stream=None) -> None:
+    """out[i] = fp16(mean over k of contribs[k][i]); flags ls on inf or NaN."""
+    n = len(contribs)
+    table = (ctypes.c_void_p * max(1, n))(*[_ptr(c, 2, f"contribs[{k}]") for k, c in enumerate(contribs)])
+    numel = out.numel() if numel is None else int(numel)
+    _check(_lib.zr_reduce_slice_f16(table, n, numel, _ptr(out, 2, "out"), _ls(ls), _stream(stream)))
+
+
+def zr_check_finite_f16(grad: torch.Tensor, ls: torch.Tensor, numel: Optional[int] = None, stream=None) -> None:
+    numel = grad.numel() if numel is None else int(numel)
+    _check(_lib.zr_check_finite_f16(_ptr(grad, 2, "grad"), numel, _ls(ls), _stream(stream)))
+
+
+def zr_adamw_step_f16(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                      param_out: Optional[torch.Tensor], ls: torch.Tensor, *, lr: float, beta1: float, beta2: float,
+                      eps: float, weight_decay: float, step: int, grad_scale: float = 1.0,
+                      numel: Optional[int] = None, stream=None) -> None:
+    """AdamW on the fp16 gradient divided by the loss scale; skipped while ls
+    holds the overflow flag."""
+    hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
+                  int(step))
+    numel = master.numel() if numel is None else int(numel)
+    _check(_lib.zr_adamw_step_f16(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                                  _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
+                                  ctypes.byref(hp), _ls(ls), _stream(stream)))
+
+
+def zr_loss_scale_update(ls: torch.Tensor, window: int = 1000, factor: float = 2.0, min_scale: float = 1.0,
+                         stream=None) -> None:
+    _check(_lib.zr_loss_scale_update(_ls(ls), int(window), float(factor), float(min_scale), _stream(stream)))
