@@ -61,6 +61,10 @@ def _load():
         lib.zr_oracle_found_inf_f16.restype = i32
         lib.zr_oracle_adamw_f16.argtypes = [p, p, p, p, p, i64, d, d, d, d, d, d, i64, d]
         lib.zr_oracle_adamw_f16.restype = None
+        lib.zr_oracle_quantize_int8.argtypes = [p, i64, i32, p, p]
+        lib.zr_oracle_quantize_int8.restype = None
+        lib.zr_oracle_dequantize_int8.argtypes = [p, p, i64, i32, p]
+        lib.zr_oracle_dequantize_int8.restype = None
         _lib = lib
     return _lib
 
@@ -265,6 +269,33 @@ def step_f16(contribs: Sequence[np.ndarray], master: np.ndarray, exp_avg: np.nda
                   weight_decay=weight_decay, step=step, loss_scale=scaler.scale, grad_scale=grad_scale)
     scaler.update(inf)
     return grad
+
+
+# ------------------------------------------------------------------ int8 ----
+
+def quantize_int8(src: np.ndarray, block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric block-wise int8 quantization of bf16 bits (the weights of the
+    quantized AllGather, ZeRO++ qwZ on the concept page (compassingai.com)):
+    per block s = amax / 127, q = rint(x / s) clamped to +-127.  Returns
+    (q int8 [numel], scales fp32 [ceil(numel / block)])."""
+    _check(src, np.uint16, "src")
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    q = np.empty(src.size, dtype=np.int8)
+    scales = np.empty(-(-src.size // block), dtype=np.float32)
+    _load().zr_oracle_quantize_int8(_ptr(src), src.size, int(block), _ptr(q), _ptr(scales))
+    return q, scales
+
+
+def dequantize_int8(q: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray:
+    """bf16 bits of q * s, rounded to nearest even."""
+    _check(q, np.int8, "q")
+    _check(scales, np.float32, "scales")
+    if scales.size != -(-q.size // block):
+        raise ValueError("scales has the wrong length")
+    out = np.empty(q.size, dtype=np.uint16)
+    _load().zr_oracle_dequantize_int8(_ptr(q), _ptr(scales), q.size, int(block), _ptr(out))
+    return out
 
 
 # ---------------------------------------------------------------- layout ----

@@ -278,3 +278,55 @@ void zr_oracle_adamw_f16(const uint16_t *grad, float *master, float *exp_avg, fl
             param_out[i] = f32_to_f16(master[i]);
     }
 }
+
+/* ------------------------------------------------- int8 block quantizing ---- */
+
+/*
+ * Quantized weights for the parameter AllGather (ZeRO++ qwZ): the ZeRO-1/2/3
+ * concept page (compassingai.com), ZeRO++ section, quantizes the weights sent
+ * in the AllGather to int8 (or int4) to cut its volume, and leaves the details
+ * to DeepSpeed.  Reading taken: symmetric block-wise int8.  For each block of
+ * `block` consecutive elements (the last block may be shorter):
+ *   amax  = max |x|                       (fp32, exact)
+ *   s     = amax / 127                    (one fp32 division)
+ *   q     = 0 if s == 0, else rint(x / s) (fp32 division, ties to even),
+ *           clamped to [-127, 127]
+ * and the receiver rebuilds x' = bf16(q * s) (one fp32 product, then bf16
+ * round to nearest even).  Inputs are finite.
+ */
+void zr_oracle_quantize_int8(const uint16_t *src, int64_t numel, int32_t block, int8_t *q, float *scales)
+{
+    int64_t nblocks = (numel + block - 1) / block;
+    for (int64_t b = 0; b < nblocks; ++b) {
+        int64_t lo = b * block;
+        int64_t hi = lo + block < numel ? lo + block : numel;
+        float amax = 0.0f;
+        for (int64_t i = lo; i < hi; ++i) {
+            float a = fabsf(bf16_to_f32(src[i]));
+            if (a > amax)
+                amax = a;
+        }
+        float s = amax / 127.0f;
+        scales[b] = s;
+        for (int64_t i = lo; i < hi; ++i) {
+            if (s == 0.0f) {
+                q[i] = 0;
+                continue;
+            }
+            float r = rintf(bf16_to_f32(src[i]) / s);
+            if (r > 127.0f)
+                r = 127.0f;
+            if (r < -127.0f)
+                r = -127.0f;
+            q[i] = (int8_t)r;
+        }
+    }
+}
+
+void zr_oracle_dequantize_int8(const int8_t *q, const float *scales, int64_t numel, int32_t block, uint16_t *dst)
+{
+    for (int64_t i = 0; i < numel; ++i) {
+        float x = (float)q[i] * scales[i / block];
+        dst[i] = f32_to_bf16(x);
+    }
+}

@@ -45,12 +45,18 @@ MUTATIONS = [
     ("overflowing step not skipped", PY, "    if not inf:\n        adamw_f16(", "    if True:\n        adamw_f16("),
     ("backoff ignores the floor", PY, "self.scale = max(self.scale / self.factor, self.min_scale)",
      "self.scale = self.scale / self.factor"),
+    ("int8 ties away from zero", C, "float r = rintf(bf16_to_f32(src[i]) / s);",
+     "float r = roundf(bf16_to_f32(src[i]) / s);"),
+    ("int8 scale over 128", C, "float s = amax / 127.0f;", "float s = amax / 128.0f;"),
+    ("int8 absmax without abs", C, "float a = fabsf(bf16_to_f32(src[i]));", "float a = bf16_to_f32(src[i]);"),
+    ("int8 dequant wrong block", C, "float x = (float)q[i] * scales[i / block];",
+     "float x = (float)q[i] * scales[(i + 1) / block < (numel + block - 1) / block ? (i + 1) / block : i / block];"),
     ("unpack reversed", PY, "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n]",
      "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n][::-1]"),
 ]
 
 PIN_TESTS = ["tests/test_oracle_numerics.py", "tests/test_oracle_layout.py", "tests/test_oracle_ledger.py",
-             "tests/test_oracle_fp16.py"]
+             "tests/test_oracle_fp16.py", "tests/test_oracle_int8.py"]
 
 
 @pytest.mark.parametrize("what,path,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
