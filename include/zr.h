@@ -10,8 +10,10 @@
  *   3. a fused mixed-precision AdamW step on the slice (zr_adamw_step)
  *   4. bit copies between per-tensor bf16 views and the flat buffer
  *                                                    (zr_pack / zr_unpack)
- * and 2 + 3 in one pass (zr_reduce_adamw_step), and an fp16 variant of 2 + 3
- * with dynamic loss scaling (zr_*_f16, zr_loss_scale_*).
+ * and 2 + 3 in one pass (zr_reduce_adamw_step), an fp16 variant of 2 + 3
+ * with dynamic loss scaling (zr_*_f16, zr_loss_scale_*), and int8 block
+ * quantization of the bf16 shard for a quantized parameter AllGather
+ * (zr_quantize_int8 / zr_dequantize_int8).
  *
  * Sources are web pages on DeepSpeed ZeRO-3, cited by title and section:
  *   [ENC]  "DeepSpeed ZeRO-3", encyclopedia entry (baike.kuaisou.com)
@@ -327,6 +329,37 @@ ZR_API zr_status zr_adamw_step_f16(const void *grad, float *master, float *exp_a
  * > 1, min_scale finite and > 0.  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP. */
 ZR_API zr_status zr_loss_scale_update(zr_loss_scale *ls, int32_t window, float factor, float min_scale,
                                       void *stream);
+
+/* ------------------------------------------------- int8 weight gather ---- */
+
+/*
+ * Quantized parameter AllGather: before the gather the rank turns its bf16
+ * parameter shard into int8 codes plus one fp32 scale per block (about 1 byte
+ * per element instead of 2), and after it every rank turns the gathered codes
+ * back into bf16.  [CON] ZeRO++ section (qwZ: the weights carried by the
+ * AllGather are quantized to int8 or int4 to cut its volume; the scheme is left
+ * to DeepSpeed); [ENC] history section (ZeRO++ as the follow-up that reduces
+ * communication volume).  Reading taken: symmetric, block-wise, per block of
+ * `block` consecutive elements (the last block may be shorter):
+ *   amax = max |x|, s = amax / 127 (fp32), q = rint(x / s) clamped to
+ *   [-127, 127] (ties to even; q = 0 when s = 0);  x' = bf16(q * s)
+ * with every division and product one fp32 operation, so the codes, scales and
+ * rebuilt values are exact functions of the input bits.  The input must be
+ * finite.
+ *
+ * block is 256, 512, 1024 or 2048.  scales has ceil(numel / block) fp32
+ * entries.  bf16 buffers need 2-byte and scales 4-byte alignment (else
+ * ZR_EALIGN); q has no alignment rule, and buffers that are 8-byte (bf16) and
+ * 4-byte (int8) aligned take the vector path (same bits).  No two buffers may
+ * overlap.  numel == 0 is a no-op.  Errors: ZR_EINVAL, ZR_EALIGN, ZR_ERANGE,
+ * ZR_EHIP.
+ */
+ZR_API zr_status zr_quantize_int8(const void *src, int64_t numel, int32_t block, int8_t *q, float *scales,
+                                  void *stream);
+
+/* Rebuilds bf16 dst[numel] from the codes and scales of zr_quantize_int8. */
+ZR_API zr_status zr_dequantize_int8(const int8_t *q, const float *scales, int64_t numel, int32_t block, void *dst,
+                                    void *stream);
 
 /* ------------------------------------------------------------- misc ------ */
 

@@ -15,6 +15,7 @@ import torch
 GUARD = 64
 GUARD_U16 = 0x5A5A
 GUARD_F32_BITS = 0x7FBADBAD  # a NaN pattern nobody computes
+GUARD_I8 = -128  # outside the int8 code range [-127, 127]
 
 
 def device():
@@ -50,6 +51,10 @@ class Placed:
             big = torch.from_numpy(np.full(offset + n + GUARD, GUARD_F32_BITS, dtype=np.uint32).view(np.float32))
             big[offset:offset + n] = torch.from_numpy(host.copy())
             self.guard_bits = np.uint32(GUARD_F32_BITS)
+        elif host.dtype == np.int8:
+            big = torch.full((offset + n + GUARD,), GUARD_I8, dtype=torch.int8)
+            big[offset:offset + n] = torch.from_numpy(host.copy())
+            self.guard_bits = np.int8(GUARD_I8)
         else:
             raise TypeError(host.dtype)
         self.big = big.to(dev)
@@ -59,11 +64,14 @@ class Placed:
     def host(self) -> np.ndarray:
         if self.view.dtype == torch.int16:
             return u16(self.view)
+        if self.view.dtype == torch.int8:
+            return self.view.cpu().numpy().copy()
         return f32(self.view)
 
     def guards_intact(self) -> bool:
         b = self.big.cpu().numpy()
-        b = b.view(np.uint16) if b.dtype == np.int16 else b.view(np.uint32)
+        if b.dtype != np.int8:
+            b = b.view(np.uint16) if b.dtype == np.int16 else b.view(np.uint32)
         return bool(np.all(b[:self.offset] == self.guard_bits) and np.all(b[self.offset + self.n:] == self.guard_bits))
 
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 21
     lib = ctypes.CDLL(zr.LIBRARY)
     for name in names:
         assert hasattr(lib, name), name
@@ -327,3 +327,41 @@ def test_fp16_validation():
     assert L.zr_adamw_step_f16(A, A + 2**22 + 2, *args[2:], 16, ctypes.byref(hp), ls, None) == zr.ZR_EALIGN
     assert L.zr_adamw_step_f16(*args, 16, ctypes.byref(hp), A + 2**23 + 16, None) == zr.ZR_EINVAL  # record in m
     assert L.zr_adamw_step_f16(*args, 0, ctypes.byref(hp), ls, None) == zr.ZR_OK
+
+
+def test_int8_validation():
+    L = zr._lib
+    src, q, sc, dst = A, A + 2**22, A + 2**23, A + 2**24
+    for block in (0, 1, 128, 300, 4096, -256):
+        assert L.zr_quantize_int8(src, 1000, block, q, sc, None) == zr.ZR_EINVAL
+        assert L.zr_dequantize_int8(q, sc, 1000, block, dst, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int8(src, -1, 256, q, sc, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int8(None, 16, 256, q, sc, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int8(src, 16, 256, None, sc, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int8(src, 16, 256, q, None, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int8(src + 1, 16, 256, q, sc, None) == zr.ZR_EALIGN
+    assert L.zr_quantize_int8(src, 16, 256, q, sc + 2, None) == zr.ZR_EALIGN
+    assert L.zr_quantize_int8(src, 1000, 256, src + 1000, sc, None) == zr.ZR_EINVAL     # codes inside src
+    assert L.zr_quantize_int8(src, 1000, 256, q, q + 996, None) == zr.ZR_EINVAL         # scales over the codes' tail
+    assert L.zr_quantize_int8(src, 0, 256, q, sc, None) == zr.ZR_OK
+    assert L.zr_quantize_int8(None, 0, 256, None, None, None) == zr.ZR_OK
+    assert L.zr_dequantize_int8(q, sc, -1, 256, dst, None) == zr.ZR_EINVAL
+    assert L.zr_dequantize_int8(q, sc, 16, 256, None, None) == zr.ZR_EINVAL
+    assert L.zr_dequantize_int8(None, sc, 16, 256, dst, None) == zr.ZR_EINVAL
+    assert L.zr_dequantize_int8(q, sc, 16, 256, dst + 1, None) == zr.ZR_EALIGN
+    assert L.zr_dequantize_int8(q, sc + 1, 16, 256, dst, None) == zr.ZR_EALIGN
+    assert L.zr_dequantize_int8(q, sc, 1000, 256, q - 1000, None) == zr.ZR_EINVAL       # dst over the codes' head
+    assert L.zr_dequantize_int8(q, sc, 0, 256, dst, None) == zr.ZR_OK
+
+
+
+def test_int8_binding_checks_buffer_sizes():
+    src = torch.zeros(1000, dtype=torch.int16)
+    with pytest.raises(ValueError):
+        zr.zr_quantize_int8(src, torch.zeros(999, dtype=torch.int8), torch.zeros(4, dtype=torch.float32), block=256)
+    with pytest.raises(ValueError):
+        zr.zr_quantize_int8(src, torch.zeros(1000, dtype=torch.int8), torch.zeros(3, dtype=torch.float32), block=256)
+    with pytest.raises(TypeError):
+        zr.zr_quantize_int8(src, torch.zeros(1000, dtype=torch.int16), torch.zeros(4, dtype=torch.float32), block=256)
+    with pytest.raises(ValueError):
+        zr.zr_dequantize_int8(torch.zeros(1000, dtype=torch.int8), torch.zeros(1, dtype=torch.float32), src, block=512)

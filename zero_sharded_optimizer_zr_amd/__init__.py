@@ -83,6 +83,8 @@ _SIGS = {
     "zr_check_finite_f16": ([_P, _I64, _P, _P], _I32),
     "zr_adamw_step_f16": ([_P, _P, _P, _P, _P, _I64, _P, _P, _P], _I32),
     "zr_loss_scale_update": ([_P, _I32, ctypes.c_float, ctypes.c_float, _P], _I32),
+    "zr_quantize_int8": ([_P, _I64, _I32, _P, _P, _P], _I32),
+    "zr_dequantize_int8": ([_P, _P, _I64, _I32, _P, _P], _I32),
     "zr_last_error": ([], ctypes.c_char_p),
     "zr_abi_version": ([], _I32),
 }
@@ -321,3 +323,31 @@ def zr_adamw_step_f16(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.T
 def zr_loss_scale_update(ls: torch.Tensor, window: int = 1000, factor: float = 2.0, min_scale: float = 1.0,
                          stream=None) -> None:
     _check(_lib.zr_loss_scale_update(_ls(ls), int(window), float(factor), float(min_scale), _stream(stream)))
+
+
+# ---------------------------------------------------------- int8 gather ----
+
+def _int8_sizes(numel: int, block: int, q: torch.Tensor, scales: torch.Tensor):
+    if q.numel() < numel:
+        raise ValueError(f"q holds {q.numel()} elements, {numel} needed")
+    if block > 0 and scales.numel() < -(-numel // block):
+        raise ValueError(f"scales holds {scales.numel()} entries, {-(-numel // block)} needed")
+
+
+def zr_quantize_int8(src: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, block: int = 2048,
+                     numel: Optional[int] = None, stream=None) -> None:
+    """Per block of `block` elements of bf16 src: scales[b] = amax / 127 and
+    q[i] = rint(src[i] / scales[b]) clamped to +-127."""
+    numel = src.numel() if numel is None else int(numel)
+    _int8_sizes(numel, int(block), q, scales)
+    _check(_lib.zr_quantize_int8(_ptr(src, 2, "src"), numel, int(block), _ptr(q, 1, "q"),
+                                 _ptr(scales, 4, "scales"), _stream(stream)))
+
+
+def zr_dequantize_int8(q: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor, block: int = 2048,
+                       numel: Optional[int] = None, stream=None) -> None:
+    """dst[i] = bf16(q[i] * scales[i // block])."""
+    numel = dst.numel() if numel is None else int(numel)
+    _int8_sizes(numel, int(block), q, scales)
+    _check(_lib.zr_dequantize_int8(_ptr(q, 1, "q"), _ptr(scales, 4, "scales"), numel, int(block),
+                                   _ptr(dst, 2, "dst"), _stream(stream)))
