@@ -443,3 +443,51 @@ def unpack(layout: Layout, flat: np.ndarray, begin: int, end: int, views: Sequen
     for t, toff, foff, n in layout.fragments(begin, end):
         arr, first = views[t]
         arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n]
+
+
+# ------------------------------------------------- quantized weight gather ----
+
+def quantize_gathered(layout: Layout, flat: np.ndarray, block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The quantized AllGather of the whole flat buffer (bf16 bits of
+    [0, psi_pad)): every rank r quantizes its own shard flat[r S, (r+1) S) by
+    quantize_int8 -- blocks start afresh at every shard, and a shard's last
+    block is short when the block size does not divide S -- and the gather
+    concatenates codes and scales in rank order (ceil(S / block) scales per
+    rank).  ZeRO++ qwZ on the concept page (compassingai.com): the weights
+    cross the AllGather quantized."""
+    _check(flat, np.uint16, "flat")
+    if flat.size != layout.psi_pad:
+        raise ValueError("flat must hold psi_pad elements")
+    S = layout.shard
+    codes, scales = [], []
+    for r in range(layout.n_d):
+        q, s = quantize_int8(np.ascontiguousarray(flat[r * S:(r + 1) * S]), block)
+        codes.append(q)
+        scales.append(s)
+    return np.concatenate(codes), np.concatenate(scales)
+
+
+def gathered_block(layout: Layout, i: np.ndarray, block: int) -> np.ndarray:
+    """Index into the gathered scales of the block that holds flat element i:
+    rank r = i // S, then block (i - r S) // block of that rank's shard."""
+    S = layout.shard
+    per_rank = -(-S // block)
+    r = i // S
+    return r * per_rank + (i - r * S) // block
+
+
+def unpack_int8(layout: Layout, q: np.ndarray, scales: np.ndarray, block: int, begin: int, end: int,
+                views: Sequence[View]) -> None:
+    """Receiver side of the quantized AllGather: flat elements [begin, end) are
+    rebuilt as bf16(code * scale of their block) and scattered into the views
+    like unpack.  q[k] is the code of flat element begin + k; scales[0] is the
+    scale of the block holding element begin, and the rest follow in gathered
+    order."""
+    _check(q, np.int8, "q")
+    _check(scales, np.float32, "scales")
+    if end <= begin:
+        return
+    i = np.arange(begin, end, dtype=np.int64)
+    g = gathered_block(layout, i, block)
+    x = q[: end - begin].astype(np.float32) * scales[g - g[0]]
+    unpack(layout, bf16_from_f32(x), begin, end, views)

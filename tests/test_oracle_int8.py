@@ -97,3 +97,94 @@ def test_exact_ties_round_to_even():
         q, s, _ = rt(x, 8)
         assert s[0] == np.float32(2.0 ** -e)
         assert list(q) == [127, 0, 2, 2, -2, 126, 0, 4]
+
+
+# ------------------------------------------- the gathered, per-shard blocks ----
+
+def _flat_with_block_magnitudes(layout, block, seed):
+    """bf16 flat buffer whose blocks (of the shard-relative grid) have very
+    different magnitudes, so that a wrong scale for an element shows."""
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 1, layout.psi_pad)
+    x *= 2.0 ** rng.integers(-12, 12, size=layout.psi_pad // 64 + 1).repeat(64)[: layout.psi_pad]
+    x[layout.psi_part:] = 0.0                          # the padding is zero
+    return bf16(x)
+
+
+def test_gathered_equals_one_grid_when_block_divides_shard():
+    lay = oracle.Layout([300_000, 50, 211_000, 120_000], n_d=4)
+    block = 256
+    pad = (-lay.psi_part) % (4 * block)                # make S a multiple of the block
+    lay = oracle.Layout([300_000, 50, 211_000, 120_000 + pad], n_d=4)
+    assert lay.shard % block == 0
+    flat = _flat_with_block_magnitudes(lay, block, 1)
+    q, s = oracle.quantize_gathered(lay, flat, block)
+    q1, s1 = oracle.quantize_int8(flat, block)
+    assert np.array_equal(q, q1) and np.array_equal(s, s1)
+
+
+def test_gathered_blocks_restart_at_every_shard():
+    lay = oracle.Layout([200_003, 7, 150_001], n_d=3)
+    block = 512
+    S = lay.shard
+    assert S % block != 0
+    flat = _flat_with_block_magnitudes(lay, block, 2)
+    q, s = oracle.quantize_gathered(lay, flat, block)
+    per_rank = -(-S // block)
+    assert s.size == 3 * per_rank and q.size == lay.psi_pad
+    xf = np.abs(oracle.f32_from_bf16(flat))
+    for r in range(3):
+        for j in (0, 1, per_rank - 2, per_rank - 1):
+            lo, hi = r * S + j * block, min(r * S + (j + 1) * block, (r + 1) * S)
+            assert s[r * per_rank + j] == np.float32(xf[lo:hi].max()) / np.float32(127)
+    assert S - (per_rank - 1) * block < block           # every shard ends with a short block
+
+
+def _views_for(lay, seed, fill=0x7777):
+    rng = np.random.default_rng(seed)
+    views = []
+    for t, n in enumerate(lay.numels):
+        if lay.persistent[t]:
+            views.append(None)
+        else:
+            views.append((np.full(n, fill, np.uint16), 0))
+    return views
+
+
+@pytest.mark.parametrize("block", [256, 2048])
+def test_unpack_int8_error_bound_per_element(block):
+    lay = oracle.Layout([200_003, 7, 150_001, 99_999, 130_000], n_d=3)
+    flat = _flat_with_block_magnitudes(lay, block, block)
+    q, s = oracle.quantize_gathered(lay, flat, block)
+    views = _views_for(lay, 0)
+    oracle.unpack_int8(lay, q, s, block, 0, lay.psi_pad, views)
+    back = oracle.pack(lay, views, 0, lay.psi_pad)
+    i = np.arange(lay.psi_part)
+    sc = s[oracle.gathered_block(lay, i, block)].astype(np.float64)
+    xf = oracle.f32_from_bf16(flat[: lay.psi_part]).astype(np.float64)
+    bf = oracle.f32_from_bf16(back[: lay.psi_part]).astype(np.float64)
+    assert np.all(np.abs(bf - xf) <= sc * (0.5 + 1e-5) + np.abs(bf) * 2.0 ** -8)
+    # and the scale really is the block's own: each rebuilt element is a code times it
+    qq = q[: lay.psi_part].astype(np.float64)
+    assert np.array_equal(back[: lay.psi_part], bf16((qq * sc).astype(np.float32)))
+
+
+def test_unpack_int8_subranges_match_the_full_range():
+    lay = oracle.Layout([200_003, 7, 150_001, 99_999, 130_000], n_d=3)
+    block = 256
+    S = lay.shard
+    flat = _flat_with_block_magnitudes(lay, block, 5)
+    q, s = oracle.quantize_gathered(lay, flat, block)
+    full = _views_for(lay, 0)
+    oracle.unpack_int8(lay, q, s, block, 0, lay.psi_pad, full)
+    for begin, end in [(0, 1000), (S - 300, S + 300), (S + 100, 2 * S + 7), (777, lay.psi_pad), (2 * S - 1, 2 * S + 1)]:
+        part = _views_for(lay, 0)
+        g0 = int(oracle.gathered_block(lay, np.array([begin]), block)[0])
+        oracle.unpack_int8(lay, q[begin:end].copy(), s[g0:].copy(), block, begin, end, part)
+        for t, toff, foff, n in lay.fragments(begin, end):
+            assert np.array_equal(part[t][0][toff:toff + n], full[t][0][toff:toff + n]), (begin, end, t)
+        # nothing outside the range is written
+        touched = {t for t, *_ in lay.fragments(begin, end)}
+        for t, v in enumerate(part):
+            if v is not None and t not in touched:
+                assert np.all(v[0] == 0x7777)

@@ -51,6 +51,10 @@ MUTATIONS = [
     ("int8 absmax without abs", C, "float a = fabsf(bf16_to_f32(src[i]));", "float a = bf16_to_f32(src[i]);"),
     ("int8 dequant wrong block", C, "float x = (float)q[i] * scales[i / block];",
      "float x = (float)q[i] * scales[(i + 1) / block < (numel + block - 1) / block ? (i + 1) / block : i / block];"),
+    ("gathered blocks not restarted per shard", PY, "return r * per_rank + (i - r * S) // block",
+     "return i // block"),
+    ("sub-range scales not offset", PY, "x = q[: end - begin].astype(np.float32) * scales[g - g[0]]",
+     "x = q[: end - begin].astype(np.float32) * scales[g - g[0] + (1 if begin > 0 else 0)]"),
     ("unpack reversed", PY, "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n]",
      "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n][::-1]"),
 ]
