@@ -13,7 +13,7 @@
  * and 2 + 3 in one pass (zr_reduce_adamw_step), an fp16 variant of 2 + 3
  * with dynamic loss scaling (zr_*_f16, zr_loss_scale_*), and int8 block
  * quantization of the bf16 shard for a quantized parameter AllGather
- * (zr_quantize_int8 / zr_dequantize_int8).
+ * (zr_quantize_int8 / zr_dequantize_int8 / zr_unpack_int8).
  *
  * Sources are web pages on DeepSpeed ZeRO-3, cited by title and section:
  *   [ENC]  "DeepSpeed ZeRO-3", encyclopedia entry (baike.kuaisou.com)
@@ -360,6 +360,28 @@ ZR_API zr_status zr_quantize_int8(const void *src, int64_t numel, int32_t block,
 /* Rebuilds bf16 dst[numel] from the codes and scales of zr_quantize_int8. */
 ZR_API zr_status zr_dequantize_int8(const int8_t *q, const float *scales, int64_t numel, int32_t block, void *dst,
                                     void *stream);
+
+/*
+ * Dequantize-on-unpack for the quantized AllGather over the partition: every
+ * rank r quantizes its shard, flat elements [r S, (r+1) S), with
+ * zr_quantize_int8 -- so blocks restart at every shard, and a shard's last
+ * block is short when `block` does not divide S -- and the gather concatenates
+ * codes and scales in rank order (ceil(S / block) scales per rank).  This call
+ * rebuilds flat elements [begin, end) as bf16(code * scale of their block) and
+ * writes them into the tensor views like zr_unpack, without a bf16 flat buffer
+ * in between.  [CON] ZeRO++ section (qwZ) and Stage 3 mechanism (parameters
+ * gathered before compute); [BLOG] "ZeRO-3: why parameters can be sharded
+ * too".
+ *
+ * q[k] is the code of flat element begin + k (end - begin bytes); scales[0] is
+ * the scale of the block that holds element begin and the following entries
+ * are the next blocks in gathered order; scales must be 4-byte aligned.  Views
+ * and their rules are those of zr_unpack (views may not overlap the codes or
+ * the scales).  Persistent tensors and the padding are not written.
+ * begin == end is a no-op.  Errors: ZR_EINVAL, ZR_ERANGE, ZR_EALIGN, ZR_EHIP.
+ */
+ZR_API zr_status zr_unpack_int8(const zr_layout *layout, const int8_t *q, const float *scales, int32_t block,
+                                int64_t begin, int64_t end, const zr_view *views, int32_t n_views, void *stream);
 
 /* ------------------------------------------------------------- misc ------ */
 

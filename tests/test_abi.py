@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 21
+    assert len(names) == 22
     lib = ctypes.CDLL(zr.LIBRARY)
     for name in names:
         assert hasattr(lib, name), name
@@ -365,3 +365,37 @@ def test_int8_binding_checks_buffer_sizes():
         zr.zr_quantize_int8(src, torch.zeros(1000, dtype=torch.int16), torch.zeros(4, dtype=torch.float32), block=256)
     with pytest.raises(ValueError):
         zr.zr_dequantize_int8(torch.zeros(1000, dtype=torch.int8), torch.zeros(1, dtype=torch.float32), src, block=512)
+
+
+def test_unpack_int8_validation():
+    lay = zr.zr_layout_create([10, 6, 3], 4, 4)  # tensor 2 persistent; psi_pad 16, shard 4
+    L = zr._lib
+    good = _views((A, 0, 10), (A + 4096, 0, 6), (None, 0, 0))
+    q, sc = A + 2**20, A + 2**21
+
+    def call(layout, qq, ss, block, b, e, views=good, n_views=3):
+        return L.zr_unpack_int8(layout, qq, ss, block, b, e, views, n_views, None)
+
+    assert call(None, q, sc, 256, 0, 16) == zr.ZR_EINVAL
+    for block in (0, 128, 300, 4096):
+        assert call(lay.handle, q, sc, block, 0, 16) == zr.ZR_EINVAL
+    assert call(lay.handle, q, sc, 256, 0, 17) == zr.ZR_ERANGE
+    assert call(lay.handle, q, sc, 256, 9, 4) == zr.ZR_ERANGE
+    assert call(lay.handle, q, sc, 256, 0, 16, n_views=2) == zr.ZR_EINVAL
+    assert call(lay.handle, q, sc, 256, 0, 16, views=None) == zr.ZR_EINVAL
+    assert call(lay.handle, None, sc, 256, 0, 16) == zr.ZR_EINVAL
+    assert call(lay.handle, q, None, 256, 0, 16) == zr.ZR_EINVAL
+    assert call(lay.handle, q, sc + 2, 256, 0, 16) == zr.ZR_EALIGN
+    assert call(lay.handle, q, q + 8, 256, 0, 16) == zr.ZR_EINVAL           # scales inside the codes
+    assert call(lay.handle, q, sc, 256, 3, 3) == zr.ZR_OK                   # empty range
+    assert call(lay.handle, None, None, 256, 3, 3) == zr.ZR_OK
+    short = _views((A, 0, 9), (A + 4096, 0, 6), (None, 0, 0))
+    assert call(lay.handle, q, sc, 256, 0, 16, views=short) == zr.ZR_ERANGE
+    missing = _views((A, 0, 10), (None, 0, 0), (None, 0, 0))
+    assert call(lay.handle, q, sc, 256, 0, 16, views=missing) == zr.ZR_EINVAL
+    odd = _views((A + 1, 0, 10), (A + 4096, 0, 6), (None, 0, 0))
+    assert call(lay.handle, q, sc, 256, 0, 16, views=odd) == zr.ZR_EALIGN
+    over_q = _views((q + 4, 0, 10), (A + 4096, 0, 6), (None, 0, 0))
+    assert call(lay.handle, q, sc, 256, 0, 16, views=over_q) == zr.ZR_EINVAL
+    over_s = _views((A, 0, 10), (sc - 4, 0, 6), (None, 0, 0))
+    assert call(lay.handle, q, sc, 256, 0, 16, views=over_s) == zr.ZR_EINVAL

@@ -184,3 +184,143 @@ def test_int8_empty_is_noop():
     zr.zr_quantize_int8(e16, e8, ef, block=256)
     zr.zr_dequantize_int8(e8, ef, e16, block=256)
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------- dequantize-on-unpack ----
+
+def _gathered_case(numels, n_d, block, seed, threshold=100_000):
+    lay = oracle.Layout(numels, n_d, threshold)
+    rng = np.random.default_rng(seed)
+    x = rng.normal(0, 1, lay.psi_pad)
+    x *= 2.0 ** rng.integers(-12, 12, size=lay.psi_pad // 64 + 1).repeat(64)[: lay.psi_pad]
+    x[lay.psi_part:] = 0.0
+    flat = bf16(x)
+    q, s = oracle.quantize_gathered(lay, flat, block)
+    return lay, q, s
+
+
+def _unpack_int8_both(lay, q, s, block, begin, end, q_off=0, view_off=3):
+    """GPU (through the C ABI, codes at byte offset q_off, views at element
+    offset view_off) and oracle results of the dequantize-on-unpack of
+    [begin, end); returns (gpu views, oracle views) as host arrays."""
+    g0 = int(oracle.gathered_block(lay, np.array([begin]), block)[0])
+    qs = np.ascontiguousarray(q[begin:end])
+    ss = np.ascontiguousarray(s[g0:])
+    placed_views, ref_views = [], []
+    for t, n in enumerate(lay.numels):
+        if lay.persistent[t]:
+            placed_views.append(None)
+            ref_views.append(None)
+            continue
+        init = np.full(n, 0x7777, np.uint16)
+        placed_views.append(Placed(init, view_off + t % 5))
+        ref_views.append((init.copy(), 0))
+    pq = Placed(qs, q_off)
+    ps = Placed(ss, 0)
+    glay = zr.zr_layout_create(lay.numels, lay.n_d, lay.threshold)
+    zr.zr_unpack_int8(glay, pq.view, ps.view, begin, end, [p.view if p else None for p in placed_views], block=block)
+    torch.cuda.synchronize()
+    oracle.unpack_int8(lay, qs, ss, block, begin, end, ref_views)
+    assert pq.guards_intact() and ps.guards_intact()
+    got = []
+    for p in placed_views:
+        if p is not None:
+            assert p.guards_intact()
+        got.append(None if p is None else p.host())
+    return got, [None if v is None else v[0] for v in ref_views]
+
+
+@pytest.mark.parametrize("block", BLOCKS)
+@pytest.mark.parametrize("n_d", [1, 3, 4])
+def test_unpack_int8_full_range_matches_oracle(block, n_d):
+    device()
+    numels = [200_003, 7, 150_001, 99_999, 130_000, 5, 311_111]
+    say("unpack_int8 full range block", block, "n_d", n_d)
+    lay, q, s = _gathered_case(numels, n_d, block, block + n_d)
+    got, ref = _unpack_int8_both(lay, q, s, block, 0, lay.psi_pad)
+    for t, (g, r) in enumerate(zip(got, ref)):
+        if g is not None:
+            assert_bits_equal(g, r, f"tensor {t} block {block} n_d {n_d}")
+
+
+@pytest.mark.parametrize("q_off,view_off", [(0, 0), (1, 0), (5, 3), (7, 1), (4, 4)])
+def test_unpack_int8_misaligned_codes_and_views(q_off, view_off):
+    device()
+    numels = [120_017, 50_003, 170_001]
+    block = 512
+    lay, q, s = _gathered_case(numels, 3, block, 11)
+    got, ref = _unpack_int8_both(lay, q, s, block, 0, lay.psi_pad, q_off, view_off)
+    for t, (g, r) in enumerate(zip(got, ref)):
+        if g is not None:
+            assert_bits_equal(g, r, f"tensor {t} offsets {q_off}/{view_off}")
+
+
+def test_unpack_int8_subranges_and_short_shard_blocks():
+    device()
+    block = 256
+    # shard = 113_335 elements: 442 full blocks and a last block of 183 per shard
+    numels = [200_003, 150_001, 90_000, 13]
+    lay, q, s = _gathered_case(numels, 4, block, 3, threshold=50)
+    S = lay.shard
+    for begin, end in [(0, 1000), (S - 300, S + 300), (S + 100, 2 * S + 7), (777, lay.psi_pad),
+                       (2 * S - 1, 2 * S + 1), (3 * S - 183, 3 * S - 180), (5, 6), (0, lay.psi_part)]:
+        got, ref = _unpack_int8_both(lay, q, s, block, begin, end)
+        for t, (g, r) in enumerate(zip(got, ref)):
+            if g is not None:
+                assert_bits_equal(g, r, f"tensor {t} range [{begin}, {end})")
+
+
+def test_unpack_int8_equals_dequantize_then_unpack_on_gpu():
+    """The fused path gives the same bits as dequantizing each rank's shard
+    into a flat bf16 buffer and unpacking it."""
+    dev = device()
+    numels = [300_001, 70_003, 250_000]
+    block = 1024
+    lay, q, s = _gathered_case(numels, 4, block, 21)
+    S, per_rank = lay.shard, -(-lay.shard // block)
+    qd = torch.from_numpy(q).to(dev)
+    sd = torch.from_numpy(s).to(dev)
+    flat = torch.empty(lay.psi_pad, dtype=torch.int16, device=dev)
+    for r in range(4):
+        zr.zr_dequantize_int8(qd[r * S:(r + 1) * S], sd[r * per_rank:(r + 1) * per_rank],
+                              flat[r * S:(r + 1) * S], block=block)
+    glay = zr.zr_layout_create(numels, 4)
+    a = [torch.full((n,), 0x1234, dtype=torch.int16, device=dev) for n in numels]
+    b = [torch.full((n,), 0x1234, dtype=torch.int16, device=dev) for n in numels]
+    zr.zr_unpack(glay, flat, 0, lay.psi_pad, a)
+    zr.zr_unpack_int8(glay, qd, sd, 0, lay.psi_pad, b, block=block)
+    torch.cuda.synchronize()
+    for t in range(3):
+        assert torch.equal(a[t], b[t]), t
+
+
+def test_unpack_int8_full_size_7b_over_4_ranks_sampled():
+    """The gathered codes of a 7e9-parameter tensor over 4 ranks (7 GB of codes,
+    14 GB of bf16 output) rebuilt in one call; sampled windows are recomputed by
+    the oracle from the same codes and scales."""
+    dev = device()
+    w = FLAT_7B
+    block = 2048
+    lay = oracle.Layout(w.numels, w.n_d)
+    S, per_rank = lay.shard, -(-lay.shard // block)
+    say("unpack_int8 full size psi_pad", lay.psi_pad, "shard", S)
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    qd = torch.randint(-127, 128, (lay.psi_pad,), dtype=torch.int8, device=dev, generator=g)
+    sd = torch.rand(w.n_d * per_rank, dtype=torch.float32, device=dev, generator=g) * 1e-3
+    out = torch.empty(w.numels[0], dtype=torch.int16, device=dev)
+    glay = zr.zr_layout_create(w.numels, w.n_d)
+    zr.zr_unpack_int8(glay, qd, sd, 0, lay.psi_pad, [out], block=block)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    starts = np.concatenate([rng.integers(0, lay.psi_part - 4096, 300), [0, S - 2000, 2 * S - 7, lay.psi_part - 4096]])
+    sh = sd.cpu().numpy()
+    for b0 in starts:
+        b0 = int(b0)
+        b1 = b0 + 4096
+        g0 = int(oracle.gathered_block(lay, np.array([b0]), block)[0])
+        ref = (np.full(4096, 0, np.uint16), b0)
+        oracle.unpack_int8(lay, qd[b0:b1].cpu().numpy(), sh[g0:g0 + 8].copy(), block, b0, b1, [ref])
+        assert_bits_equal(out[b0:b1].cpu().numpy().view(np.uint16), ref[0], f"window at {b0}")
+    del qd, sd, out
+    torch.cuda.empty_cache()

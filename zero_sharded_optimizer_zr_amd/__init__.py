@@ -85,6 +85,7 @@ _SIGS = {
     "zr_loss_scale_update": ([_P, _I32, ctypes.c_float, ctypes.c_float, _P], _I32),
     "zr_quantize_int8": ([_P, _I64, _I32, _P, _P, _P], _I32),
     "zr_dequantize_int8": ([_P, _P, _I64, _I32, _P, _P], _I32),
+    "zr_unpack_int8": ([_P, _P, _P, _I32, _I64, _I64, _P, _I32, _P], _I32),
     "zr_last_error": ([], ctypes.c_char_p),
     "zr_abi_version": ([], _I32),
 }
@@ -143,7 +144,8 @@ class Layout:
         return self._h
 
     def __del__(self):
-        if getattr(self, "_h", None) and self._h.value:
+        # at interpreter exit the module's globals may already be gone
+        if getattr(self, "_h", None) and self._h.value and _lib is not None:
             _lib.zr_layout_destroy(self._h)
             self._h = ctypes.c_void_p(None)
 
@@ -351,3 +353,15 @@ def zr_dequantize_int8(q: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor,
     _int8_sizes(numel, int(block), q, scales)
     _check(_lib.zr_dequantize_int8(_ptr(q, 1, "q"), _ptr(scales, 4, "scales"), numel, int(block),
                                    _ptr(dst, 2, "dst"), _stream(stream)))
+
+
+def zr_unpack_int8(layout: Layout, q: torch.Tensor, scales: torch.Tensor, begin: int, end: int,
+                   views: Sequence[ViewArg], block: int = 2048, stream=None) -> None:
+    """Per-tensor views <- bf16(code * scale) for flat elements [begin, end) of
+    a quantized AllGather (per-shard blocks); q[k] is the code of element
+    begin + k and scales[0] the scale of the block holding element begin."""
+    if q.numel() < end - begin:
+        raise ValueError(f"q holds {q.numel()} codes, {end - begin} needed")
+    _check(_lib.zr_unpack_int8(layout.handle, _ptr(q, 1, "q"), _ptr(scales, 4, "scales"), int(block), int(begin),
+                               int(end), _views(layout, views), len(views), _stream(stream)))
+
