@@ -30,7 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD specification
 METRIC = "shard AdamW step elements/s + achieved HBM GB/s vs peak (7B, N_d=4 shard)"
 COUNTERS = os.path.join(ROOT, "profiles", "adamw_flat7e9_counters.json")
-KERNEL_SOURCES = ["zero_sharded_optimizer_zr_amd/csrc/adamw.hip", "zero_sharded_optimizer_zr_amd/csrc/zr_device.hpp"]
+KERNEL_SOURCES = ["zero_sharded_optimizer_zr_amd/csrc/adamw.hip", "zero_sharded_optimizer_zr_amd/csrc/zr_device.hpp",
+                  "zero_sharded_optimizer_zr_amd/csrc/zr_math.hpp"]
 
 
 def parse():
@@ -42,6 +43,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=1 << 28, help="shard prefix the oracle runs over")
     p.add_argument("--cpu-seconds", type=float, default=10.0, help="repeat the oracle step until this much time")
+    p.add_argument("--no-extra-paths", action="store_true", help="skip the fp16 and int8-gather legs")
+    p.add_argument("--qwz-block", type=int, default=2048, help="int8 block size of the quantized gather leg")
+    p.add_argument("--qwz-max-gather", type=int, default=8_000_000_000,
+                   help="largest gathered range (elements) the quantized gather leg rebuilds")
     p.add_argument("--copy-calibration", type=int, default=0,
                    help="also run N plain copies of 4 GiB (reference kernel for HBM counters)")
     return p.parse_args()
@@ -66,6 +71,42 @@ def measured_traffic(per_launch_bytes):
     if c.get("kernel_hash") != kernel_hash():
         return None
     return c.get("traffic_bytes_per_launch")
+
+
+def time_path(calls, warmup, steps, stream):
+    """Runs `calls` ([(name, fn, algorithmic bytes)]) as one step, `warmup`
+    untimed steps then `steps` timed ones, with HIP events around every call on
+    `stream`; returns (wall ms per step, {name: stats})."""
+    import numpy as np
+    import torch
+
+    def one(record):
+        evs = []
+        for name, fn, _ in calls:
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            fn()
+            if record:
+                z = torch.cuda.Event(enable_timing=True)
+                z.record(stream)
+                evs.append((a, z))
+        return evs
+
+    for _ in range(warmup):
+        one(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    rec = [one(True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps * 1e3
+    stats = {}
+    for i, (name, _, nbytes) in enumerate(calls):
+        ms = [r[i][0].elapsed_time(r[i][1]) for r in rec]
+        avg = float(np.mean(ms))
+        stats[name] = {"ms_avg": round(avg, 4), "algorithmic_bytes": nbytes,
+                       "GBps": round(nbytes / (avg * 1e-3) / 1e9, 1)}
+    return wall, stats
 
 
 def main():
@@ -233,10 +274,97 @@ def main():
                        "step_algorithmic_bytes": sum(fbytes.values()), "kernels": fkernels},
     }
 
+    if not args.no_extra_paths:
+        result["fp16_path"] = fp16_leg(w, lay, b, e, S, frags, params, st, hp, t_step, args, stream)
+        result["qwz_gather"] = qwz_leg(w, lay, info, b, S, flat_param, args, stream)
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lay, frags, b, min(args.cpu_sample, S), own_grad, contribs,
                                               st, hp, t_step, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def fp16_leg(w, lay, b, e, S, frags, params, st, hp, t_step, args, stream):
+    """The same step with fp16 gradients and dynamic loss scaling: pack of the
+    rank's own fp16 gradient, fp16 mean with the overflow flag, loss-scaled
+    AdamW (fp16 copy), the scale rule, unpack.  Gradients are scaled by the
+    initial loss scale 2^16 and stay finite, so no step is skipped."""
+    import torch
+
+    import zero_sharded_optimizer_zr_amd as zr
+    from zr_workloads import synth
+
+    dev = st["master"].device
+    scale = 2.0 ** 16
+    half = lambda k, cnt: synth.normal_f32(cnt, w.grad_std * scale, 9100 + k, dev).to(torch.float16)
+    own = [None] * len(w.numels)
+    for t, toff, _, cnt in frags:
+        own[t] = (half(t, cnt), toff)
+    contribs = [torch.empty(S, dtype=torch.float16, device=dev)] + [half(100 + k, S) for k in range(1, w.n_contrib)]
+    grad = torch.empty(S, dtype=torch.float16, device=dev)
+    param = torch.empty(S, dtype=torch.float16, device=dev)
+    master, m, v = (st[k].clone() for k in ("master", "exp_avg", "exp_avg_sq"))
+    ls = zr.loss_scale_record(dev)
+    zr.zr_loss_scale_init(ls, scale, stream=stream)
+    n = w.n_contrib
+    calls = [
+        ("pack", lambda: zr.zr_pack(lay, own, contribs[0], b, e, stream=stream), 4 * S),
+        ("reduce_f16", lambda: zr.zr_reduce_slice_f16(contribs, grad, ls, stream=stream), (2 * n + 2) * S),
+        ("adamw_f16", lambda: zr.zr_adamw_step_f16(grad, master, m, v, param, ls, step=t_step, stream=stream, **hp),
+         28 * S),
+        ("loss_scale_update", lambda: zr.zr_loss_scale_update(ls, stream=stream), 16),
+        ("unpack", lambda: zr.zr_unpack(lay, param, b, e, params, stream=stream), 4 * S),
+    ]
+    wall, stats = time_path(calls, args.warmup, args.steps, stream)
+    torch.cuda.synchronize()
+    skipped = int(ls.cpu()[3])
+    out = {"path": "pack+reduce_f16+adamw_f16+loss_scale_update+unpack", "ms_per_step": round(wall, 4),
+           "value": S / (wall * 1e-3), "unit": "elements/s", "skipped_steps": skipped, "kernels": stats}
+    del own, contribs, grad, param, master, m, v
+    torch.cuda.empty_cache()
+    return out
+
+
+def qwz_leg(w, lay, info, b, S, flat_param, args, stream):
+    """Quantized weight AllGather, local sides: this rank quantizes its updated
+    bf16 shard (zr_quantize_int8), and the gathered codes and scales of the
+    flat range [0, G) -- G = psi_pad, or at most --qwz-max-gather elements, the
+    rest of the ranks' codes synthetic -- are rebuilt straight into the bf16
+    tensor views (zr_unpack_int8).  The plain bf16 unpack of the same range
+    (zr_unpack from a bf16 flat buffer) is timed beside it."""
+    import torch
+
+    import zero_sharded_optimizer_zr_amd as zr
+
+    dev = flat_param.device
+    block = args.qwz_block
+    per_rank = -(-S // block)
+    G = min(info["psi_pad"], args.qwz_max_gather // S * S)
+    ranks = G // S
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4242)
+    codes = torch.randint(-127, 128, (G,), dtype=torch.int8, device=dev, generator=gen)
+    scales = torch.rand(ranks * per_rank, dtype=torch.float32, device=dev, generator=gen) * 1e-3
+    r = w.rank if w.rank < ranks else 0
+    my_codes, my_scales = codes[r * S:(r + 1) * S], scales[r * per_rank:(r + 1) * per_rank]
+    views = [None] * len(w.numels)
+    for t, toff, _, cnt in zr.zr_layout_fragments(lay, 0, G):
+        views[t] = (torch.empty(cnt, dtype=torch.int16, device=dev), toff)
+    flat = torch.zeros(G, dtype=torch.int16, device=dev)
+    part = min(G, info["psi_part"])
+    calls = [
+        ("quantize", lambda: zr.zr_quantize_int8(flat_param, my_codes, my_scales, block=block, stream=stream),
+         3 * S + 4 * per_rank),
+        ("unpack_int8", lambda: zr.zr_unpack_int8(lay, codes, scales, 0, G, views, block=block, stream=stream),
+         3 * part + 4 * ranks * per_rank),
+        ("unpack_bf16", lambda: zr.zr_unpack(lay, flat, 0, G, views, stream=stream), 4 * part),
+    ]
+    _, stats = time_path(calls, args.warmup, args.steps, stream)
+    out = {"block": block, "gathered_elements": G, "ranks_gathered": ranks,
+           "gather_payload_bytes": {"int8": G + 4 * ranks * per_rank, "bf16": 2 * G}, "kernels": stats}
+    del codes, scales, views, flat
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, lay, frags, b, sample, own_grad, contribs, st, hp, t_step, min_seconds):
