@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--qwz-block", type=int, default=2048, help="int8 block size of the quantized gather leg")
     p.add_argument("--qwz-max-gather", type=int, default=8_000_000_000,
                    help="largest gathered range (elements) the quantized gather leg rebuilds")
+    p.add_argument("--offload-staging-mb", type=int, default=256, help="pinned staging of the offload leg (MB)")
     p.add_argument("--copy-calibration", type=int, default=0,
                    help="also run N plain copies of 4 GiB (reference kernel for HBM counters)")
     return p.parse_args()
@@ -277,6 +278,7 @@ def main():
     if not args.no_extra_paths:
         result["fp16_path"] = fp16_leg(w, lay, b, e, S, frags, params, st, hp, t_step, args, stream)
         result["qwz_gather"] = qwz_leg(w, lay, info, b, S, flat_param, args, stream)
+        result["offload_step"] = offload_leg(w, S, grad, st, hp, t_step, args, stream)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, lay, frags, b, min(args.cpu_sample, S), own_grad, contribs,
@@ -364,6 +366,37 @@ def qwz_leg(w, lay, info, b, S, flat_param, args, stream):
            "gather_payload_bytes": {"int8": G + 4 * ranks * per_rank, "bf16": 2 * G}, "kernels": stats}
     del codes, scales, views, flat
     torch.cuda.empty_cache()
+    return out
+
+
+def offload_leg(w, S, grad, st, hp, t_step, args, stream):
+    """ZeRO-Offload step on the same shard: the bf16 gradient shard goes to the
+    host through pinned staging, the host updates fp32 master / m / v kept in
+    host memory, and the bf16 parameters come back (zr_offload_adamw_step, all
+    the process's CPUs).  Timed by the host clock: the call returns when the
+    parameters are on the device."""
+    import torch
+
+    import zero_sharded_optimizer_zr_amd as zr
+
+    host = [st[k].cpu() for k in ("master", "exp_avg", "exp_avg_sq")]
+    param = torch.empty(S, dtype=torch.int16, device=grad.device)
+    staging = zr.offload_staging(args.offload_staging_mb << 20)
+    torch.cuda.synchronize()
+    run = lambda: zr.zr_offload_adamw_step(grad, *host, param, staging, step=t_step, stream=stream, **hp)
+    for _ in range(max(1, min(args.warmup, 2))):
+        run()
+    steps = max(1, min(args.steps, 5))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        run()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    out = {"ms_per_step": round(ms, 2), "value": S / (ms * 1e-3), "unit": "elements/s", "steps": steps,
+           "host_simd": zr.zr_host_simd(), "host_threads": len(os.sched_getaffinity(0)),
+           "staging_bytes": args.offload_staging_mb << 20,
+           "pcie_bytes": 4 * S, "host_dram_bytes": 32 * S,
+           "host_dram_GBps": round(32 * S / (ms * 1e-3) / 1e9, 1)}
+    del host, param, staging
     return out
 
 

@@ -13,7 +13,9 @@
  * and 2 + 3 in one pass (zr_reduce_adamw_step), an fp16 variant of 2 + 3
  * with dynamic loss scaling (zr_*_f16, zr_loss_scale_*), and int8 block
  * quantization of the bf16 shard for a quantized parameter AllGather
- * (zr_quantize_int8 / zr_dequantize_int8 / zr_unpack_int8).
+ * (zr_quantize_int8 / zr_dequantize_int8 / zr_unpack_int8), and the
+ * ZeRO-Offload step with the optimizer on the host (zr_offload_adamw_step,
+ * zr_host_adamw_step).
  *
  * Sources are web pages on DeepSpeed ZeRO-3, cited by title and section:
  *   [ENC]  "DeepSpeed ZeRO-3", encyclopedia entry (baike.kuaisou.com)
@@ -382,6 +384,55 @@ ZR_API zr_status zr_dequantize_int8(const int8_t *q, const float *scales, int64_
  */
 ZR_API zr_status zr_unpack_int8(const zr_layout *layout, const int8_t *q, const float *scales, int32_t block,
                                 int64_t begin, int64_t end, const zr_view *views, int32_t n_views, void *stream);
+
+/* ------------------------------------------------ ZeRO-Offload step ----- */
+
+/*
+ * ZeRO-Offload: the shard's fp32 master / exp_avg / exp_avg_sq live in host
+ * memory and the AdamW update runs on the host CPU; the bf16 gradient shard
+ * crosses PCIe to the host and the bf16 parameter copy crosses back.  [TUT]
+ * 3.2 (cpu_offload moves optimizer states, gradients and even parameters to CPU
+ * memory; PCIe becomes the bottleneck); [CON] history (ZeRO-Offload: fp32
+ * optimizer states and part of the compute on the CPU); [ENC] history (ZeRO-2
+ * Offload, ZeRO-3 Offload); [ART] tuning notes (offload_optimizer to cpu).
+ *
+ * The host update performs the IEEE fp32 operations of zr_adamw_step, in the
+ * same order and on the same fp32 scalars, so it gives the same bits as the GPU
+ * kernel (AVX-512 or AVX2 chosen at run time; scalar tails).
+ */
+
+/* Smallest staging buffer zr_offload_adamw_step accepts (bytes). */
+#define ZR_OFFLOAD_MIN_STAGING 65536
+
+/*
+ * zr_adamw_step on host buffers: grad (bf16 [numel]), master / exp_avg /
+ * exp_avg_sq (fp32 [numel], in place), param_out (bf16 [numel] or NULL), all
+ * in host memory.  threads: host threads to use, 0 = every CPU the process may
+ * run on.  Synchronous.  Buffer rules as zr_adamw_step (2- and 4-byte
+ * alignment, no overlaps).  Errors: ZR_EINVAL, ZR_EALIGN.
+ */
+ZR_API zr_status zr_host_adamw_step(const void *grad, float *master, float *exp_avg, float *exp_avg_sq,
+                                    void *param_out, int64_t numel, const zr_adamw_hparams *hp, int32_t threads);
+
+/* Instruction set the host update uses: "avx512", "avx2" or "scalar". */
+ZR_API const char *zr_host_simd(void);
+
+/*
+ * The offloaded step: grad (device, bf16 [numel]) -> host AdamW on master /
+ * exp_avg / exp_avg_sq (host, fp32 [numel], in place) -> param_out (device,
+ * bf16 [numel], or NULL for no copy).  staging is caller-owned pinned host
+ * memory (hipHostMalloc), 64-byte aligned, of staging_bytes >=
+ * ZR_OFFLOAD_MIN_STAGING; the shard goes through it in chunks of
+ * staging_bytes / 8 elements (rounded down to a multiple of 64), so that the
+ * copy of one chunk overlaps the host update of the next.  Copies are enqueued
+ * on `stream`, after the work already there (e.g. the reduce that produced
+ * grad).  The call is synchronous: it returns when the states are updated and
+ * every parameter has reached the device (or, on an error, when the copies it
+ * enqueued have finished).  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
+ */
+ZR_API zr_status zr_offload_adamw_step(const void *grad, float *master, float *exp_avg, float *exp_avg_sq,
+                                       void *param_out, int64_t numel, const zr_adamw_hparams *hp, void *staging,
+                                       int64_t staging_bytes, int32_t threads, void *stream);
 
 /* ------------------------------------------------------------- misc ------ */
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 22
+    assert len(names) == 25
     lib = ctypes.CDLL(zr.LIBRARY)
     for name in names:
         assert hasattr(lib, name), name

@@ -86,6 +86,9 @@ _SIGS = {
     "zr_quantize_int8": ([_P, _I64, _I32, _P, _P, _P], _I32),
     "zr_dequantize_int8": ([_P, _P, _I64, _I32, _P, _P], _I32),
     "zr_unpack_int8": ([_P, _P, _P, _I32, _I64, _I64, _P, _I32, _P], _I32),
+    "zr_host_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _I32], _I32),
+    "zr_host_simd": ([], ctypes.c_char_p),
+    "zr_offload_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I32, _P], _I32),
     "zr_last_error": ([], ctypes.c_char_p),
     "zr_abi_version": ([], _I32),
 }
@@ -364,4 +367,62 @@ def zr_unpack_int8(layout: Layout, q: torch.Tensor, scales: torch.Tensor, begin:
         raise ValueError(f"q holds {q.numel()} codes, {end - begin} needed")
     _check(_lib.zr_unpack_int8(layout.handle, _ptr(q, 1, "q"), _ptr(scales, 4, "scales"), int(block), int(begin),
                                int(end), _views(layout, views), len(views), _stream(stream)))
+
+
+# ------------------------------------------------------------ ZeRO-Offload ----
+
+ZR_OFFLOAD_MIN_STAGING = 65536
+
+
+def _on(t: Optional[torch.Tensor], kind: str, name: str):
+    if t is not None and t.device.type != kind:
+        raise ValueError(f"{name} must be a {kind} tensor")
+
+
+def zr_host_simd() -> str:
+    """Instruction set of the host AdamW: "avx512", "avx2" or "scalar"."""
+    return _lib.zr_host_simd().decode()
+
+
+def zr_host_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                       param_out: Optional[torch.Tensor], *, lr: float, beta1: float, beta2: float, eps: float,
+                       weight_decay: float, step: int, grad_scale: float = 1.0, numel: Optional[int] = None,
+                       threads: int = 0) -> None:
+    """zr_adamw_step on host (CPU) tensors, on `threads` host threads (0: all)."""
+    for t, name in ((grad, "grad"), (master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"),
+                    (param_out, "param_out")):
+        _on(t, "cpu", name)
+    hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
+                  int(step))
+    numel = master.numel() if numel is None else int(numel)
+    _check(_lib.zr_host_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                                   _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
+                                   ctypes.byref(hp), int(threads)))
+
+
+def offload_staging(nbytes: int = 64 << 20) -> torch.Tensor:
+    """Pinned host staging buffer for zr_offload_adamw_step."""
+    return torch.empty(int(nbytes), dtype=torch.uint8, pin_memory=True)
+
+
+def zr_offload_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
+                          param_out: Optional[torch.Tensor], staging: torch.Tensor, *, lr: float, beta1: float,
+                          beta2: float, eps: float, weight_decay: float, step: int, grad_scale: float = 1.0,
+                          numel: Optional[int] = None, threads: int = 0, stream=None) -> None:
+    """ZeRO-Offload step: device bf16 grad -> host AdamW on host fp32 master /
+    exp_avg / exp_avg_sq -> device bf16 param_out, through the pinned staging
+    buffer.  Returns when the parameters are on the device."""
+    _on(grad, "cuda", "grad")
+    _on(param_out, "cuda", "param_out")
+    for t, name in ((master, "master"), (exp_avg, "exp_avg"), (exp_avg_sq, "exp_avg_sq"), (staging, "staging")):
+        _on(t, "cpu", name)
+    if not staging.is_pinned():
+        raise ValueError("staging must be pinned host memory (see offload_staging)")
+    hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
+                  int(step))
+    numel = master.numel() if numel is None else int(numel)
+    _check(_lib.zr_offload_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+                                      _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
+                                      ctypes.byref(hp), _ptr(staging, 1, "staging"), staging.numel(), int(threads),
+                                      _stream(stream)))
 

@@ -1,13 +1,15 @@
 """Builds libzr.so in-tree with hipcc for gfx950 (MI355X).
 
-Every HIP source is compiled with FP contraction off (each fp32 operation in
-the kernels is one IEEE operation, as written) and with packed-fp32 code
-generation disabled.
+Every source is compiled with FP contraction off (each fp32 operation is one
+IEEE operation, as written) and with packed-fp32 code generation disabled;
+the .hip files carry the gfx950 kernels, the .cpp files are host-only.
 """
 import glob
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -17,7 +19,7 @@ LIBRARY = os.path.join(HERE, "libzr.so")
 ARCH = "gfx950"
 
 FLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
@@ -25,15 +27,50 @@ FLAGS = [
 ]
 
 
+def device_sources():
+    """Translation units with GPU kernels (compiled for gfx950 and the host)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+
+
+def host_sources():
+    """Host-only translation units (layout, the host optimizer): no device pass,
+    so they may use host-only builtins."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
+
+
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.cpp")) + glob.glob(os.path.join(CSRC, "*.hip")))
+    return device_sources() + host_sources()
 
 
 def build(verbose: bool = False, extra=(), output: str = LIBRARY) -> str:
-    cmd = ["hipcc", *FLAGS, *extra, f"-I{INCLUDE}", f"-I{CSRC}", *sources(), "-o", output + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    """Compiles every translation unit to an object (in parallel), then links
+    libzr.so; the library is replaced only when everything succeeded."""
+    include = [f"-I{INCLUDE}", f"-I{CSRC}"]
+    with tempfile.TemporaryDirectory(prefix="zr_build_") as tmp:
+        jobs = []
+        for src in sources():
+            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            host_only = ["--offload-host-only"] if src.endswith(".cpp") else []
+            jobs.append((["hipcc", *FLAGS, *host_only, *extra, *include, "-c", src, "-o", obj], obj))
+        if verbose:
+            for cmd, _ in jobs:
+                print(" ".join(cmd), flush=True)
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+        with ThreadPoolExecutor(workers) as pool:
+            results = list(pool.map(lambda j: subprocess.run(j[0], capture_output=True, text=True), jobs))
+        failed = [(cmd, r) for (cmd, _), r in zip(jobs, results) if r.returncode != 0]
+        if verbose:
+            for r in results:
+                if r.stderr:
+                    print(r.stderr, end="", file=sys.stderr)
+        if failed:
+            cmd, r = failed[0]
+            print(r.stdout + r.stderr, file=sys.stderr)
+            raise subprocess.CalledProcessError(r.returncode, cmd)
+        link = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for _, o in jobs], "-o", output + ".tmp"]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
     os.replace(output + ".tmp", output)
     return output
 

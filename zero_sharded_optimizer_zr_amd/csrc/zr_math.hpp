@@ -66,14 +66,15 @@ struct AdamWScalars {
     float grad_scale;
 };
 
-// Decoupled-weight-decay Adam on one element, fp32, no FMA contraction.
+// Decoupled-weight-decay Adam on one element: IEEE fp32 operations (correctly
+// rounded square root and division), no FMA contraction.
 __device__ __forceinline__ void adamw_element(float graw, float &th, float &m, float &v, const AdamWScalars &s)
 {
     float g = graw * s.grad_scale;
     th = th * s.decay;
     m = s.beta1 * m + s.one_minus_beta1 * g;
     v = s.beta2 * v + (s.one_minus_beta2 * g) * g;
-    float denom = __fsqrt_rn(v) * s.inv_sqrt_bias2 + s.eps;
+    float denom = sqrt_rn(v) * s.inv_sqrt_bias2 + s.eps;
     th = th - s.step_size * __fdiv_rn(m, denom);
 }
 
