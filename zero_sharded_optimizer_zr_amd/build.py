@@ -49,7 +49,7 @@ def build(verbose: bool = False, extra=(), output: str = LIBRARY) -> str:
     with tempfile.TemporaryDirectory(prefix="zr_build_") as tmp:
         jobs = []
         for src in sources():
-            obj = os.path.join(tmp, os.path.basename(src) + ".o")
+            obj = os.path.join(tmp, os.path.basename(src).replace(".", "_") + ".o")
             host_only = ["--offload-host-only"] if src.endswith(".cpp") else []
             jobs.append((["hipcc", *FLAGS, *host_only, *extra, *include, "-c", src, "-o", obj], obj))
         if verbose:
