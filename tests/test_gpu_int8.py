@@ -324,3 +324,48 @@ def test_unpack_int8_full_size_7b_over_4_ranks_sampled():
         assert_bits_equal(out[b0:b1].cpu().numpy().view(np.uint16), ref[0], f"window at {b0}")
     del qd, sd, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("block", [256, 2048])
+def test_unpack_int8_full_size_llama_layout_sampled(block):
+    """The whole gathered buffer of the Llama-7B layout over 64 ranks (6.7e9
+    codes, 291 tensors, 65 of them persistent) rebuilt in one call; windows on
+    every tensor boundary, every shard boundary and at random places are
+    recomputed by the oracle from the same codes and scales."""
+    from zr_workloads import LLAMA_7B
+    dev = device()
+    w = LLAMA_7B
+    lay = oracle.Layout(w.numels, w.n_d, w.threshold)
+    S, per_rank = lay.shard, -(-lay.shard // block)
+    say("unpack_int8 llama layout psi_pad", lay.psi_pad, "block", block)
+    g = torch.Generator(device=dev)
+    g.manual_seed(91 + block)
+    qd = torch.randint(-127, 128, (lay.psi_pad,), dtype=torch.int8, device=dev, generator=g)
+    sd = torch.rand(w.n_d * per_rank, dtype=torch.float32, device=dev, generator=g) * 1e-2
+    views = [None if lay.persistent[t] else torch.full((n,), 0x7777, dtype=torch.int16, device=dev)
+             for t, n in enumerate(w.numels)]
+    glay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    zr.zr_unpack_int8(glay, qd, sd, 0, lay.psi_pad, views, block=block)
+    torch.cuda.synchronize()
+    sh = sd.cpu().numpy()
+    rng = np.random.default_rng(block)
+    starts = [lay.offset[t] for t in range(len(w.numels)) if not lay.persistent[t]]
+    starts += [r * S for r in range(1, w.n_d)]
+    starts = sorted({max(0, min(lay.psi_pad - 3000, x - 1500)) for x in starts} |
+                    {int(x) for x in rng.integers(0, lay.psi_pad - 3000, 200)})
+    for b0 in starts:
+        b1 = b0 + 3000
+        g0 = int(oracle.gathered_block(lay, np.array([b0]), block)[0])
+        frags = lay.fragments(b0, b1)
+        ref = [None] * len(w.numels)
+        for t, toff, foff, n in frags:
+            ref[t] = (np.zeros(n, np.uint16), toff)
+        oracle.unpack_int8(lay, qd[b0:b1].cpu().numpy(), sh[g0:g0 + 32].copy(), block, b0, b1, ref)
+        for t, toff, foff, n in frags:
+            got = views[t][toff:toff + n].cpu().numpy().view(np.uint16)
+            assert_bits_equal(got, ref[t][0], f"tensor {t} window at {b0}")
+    # the padding writes nowhere, and persistent tensors are not touched
+    assert all(v is None for v, p in zip(views, lay.persistent) if p)
+    del qd, sd, views
+    torch.cuda.empty_cache()

@@ -83,6 +83,48 @@ __device__ __forceinline__ uint32_t rebuild2(uint32_t codes, int k, float s0, fl
     return pack_bf16x2(lo, hi);
 }
 
+// The lane's chunks of tile t: every load first, then the arithmetic and the
+// stores.  kShift: the codes' byte phase differs from the destination's (two
+// words per chunk, funnel-shifted); kFull: every chunk of the tile is inside
+// the descriptor's aligned body, so no lane needs a guard.  Both are uniform
+// per workgroup.
+template <bool kShift, bool kFull>
+__device__ __forceinline__ void rebuild_chunks(const u32x2 *s2, uint32_t shift, uint16_t *out, const float *scale,
+                                               int64_t e_base, int lg, int64_t c0, int64_t body)
+{
+    u32x2 w[kPerLane], w2[kPerLane];
+    float sa[kPerLane], sb[kPerLane];
+    int32_t split[kPerLane];  // elements of the chunk in its first block
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+        const int64_t c = c0 + k * kBlock;
+        if (kFull || c < body) {
+            w[k] = load_stream(s2 + c);
+            if (kShift)
+                w2[k] = load_stream(s2 + c + 1);
+            const int64_t e0 = e_base + 8 * c;  // position of the chunk's first element in the block grid
+            const int64_t j0 = e0 >> lg;
+            sa[k] = load_global(scale + j0);
+            sb[k] = load_global(scale + ((e0 + 7) >> lg));
+            split[k] = (int32_t)(((j0 + 1) << lg) - e0);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kPerLane; ++k) {
+        const int64_t c = c0 + k * kBlock;
+        if (!kFull && c >= body)
+            break;
+        const u32x2 x = kShift ? funnel8(w[k], w2[k], shift) : w[k];
+        float s[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            s[e] = e < split[k] ? sa[k] : sb[k];
+        const u32x4 o{rebuild2(x.x, 0, s[0], s[1]), rebuild2(x.x, 2, s[2], s[3]), rebuild2(x.y, 0, s[4], s[5]),
+                      rebuild2(x.y, 2, s[6], s[7])};
+        store_stream(reinterpret_cast<u32x4 *>(out) + c, o);
+    }
+}
+
 __global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64_t total_tiles)
 {
     // grid is a multiple of kXcds; spare workgroups past the last tile exit
@@ -114,24 +156,20 @@ __global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64
     const uintptr_t s_addr = reinterpret_cast<uintptr_t>(src + head);
     const uint32_t shift = (uint32_t)(s_addr & 7);  // uniform per descriptor
     const u32x2 *s2 = reinterpret_cast<const u32x2 *>(s_addr - shift);
-#pragma unroll
-    for (int k = 0; k < kPerLane; ++k) {
-        const int64_t c = t * kTileLanes + k * kBlock + threadIdx.x;
-        if (c >= body)
-            break;
-        const int64_t k0 = head + 8 * c;  // first element of this chunk
-        const u32x2 w = shift == 0 ? load_stream(s2 + c) : funnel8(load_stream(s2 + c), load_stream(s2 + c + 1), shift);
-        const int64_t j0 = (phase + k0) >> lg;
-        const int64_t j1 = (phase + k0 + 7) >> lg;
-        const float sa = scale[j0];
-        const float sb = j1 == j0 ? sa : scale[j1];
-        float s[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            s[e] = ((phase + k0 + e) >> lg) == j0 ? sa : sb;
-        const u32x4 o{rebuild2(w.x, 0, s[0], s[1]), rebuild2(w.x, 2, s[2], s[3]), rebuild2(w.y, 0, s[4], s[5]),
-                      rebuild2(w.y, 2, s[6], s[7])};
-        store_stream(reinterpret_cast<u32x4 *>(dst + k0), o);
+    uint16_t *out = dst + head;                      // 16-byte aligned
+    const int64_t c0 = t * kTileLanes + threadIdx.x;
+    const int64_t e_base = phase + head;
+    const bool full = (t + 1) * kTileLanes <= body;
+    if (shift == 0) {
+        if (full)
+            rebuild_chunks<false, true>(s2, shift, out, scale, e_base, lg, c0, body);
+        else
+            rebuild_chunks<false, false>(s2, shift, out, scale, e_base, lg, c0, body);
+    } else {
+        if (full)
+            rebuild_chunks<true, true>(s2, shift, out, scale, e_base, lg, c0, body);
+        else
+            rebuild_chunks<true, false>(s2, shift, out, scale, e_base, lg, c0, body);
     }
 
     if (t == 0) {

@@ -15,18 +15,33 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlock = 256;  // 4 wave64 per workgroup
 
+// Every buffer the kernels touch is in global memory.  Pointers that arrive
+// through a descriptor table (not as kernel arguments) are generic to the
+// compiler, which then emits flat instructions (counted against both the
+// vector-memory and the scalar/LDS counters); casting to the global address
+// space gives global_load / global_store with scalar-base addressing.
+template <typename T>
+using global_ptr = __attribute__((address_space(1))) T *;
+
 // Streaming accesses: every byte is touched once, so loads and stores carry the
 // non-temporal hint (the caches do not keep the line for reuse).
 template <typename T>
 __device__ __forceinline__ T load_stream(const T *p)
 {
-    return __builtin_nontemporal_load(p);
+    return __builtin_nontemporal_load((global_ptr<const T>)p);
 }
 
 template <typename T>
 __device__ __forceinline__ void store_stream(T *p, T v)
 {
-    __builtin_nontemporal_store(v, p);
+    __builtin_nontemporal_store(v, (global_ptr<T>)p);
+}
+
+// Ordinary (cached) global load, for data that neighbouring lanes share.
+template <typename T>
+__device__ __forceinline__ T load_global(const T *p)
+{
+    return *(global_ptr<const T>)p;
 }
 
 // bf16 -> fp32 is exact: the 16 bits are the upper half of the fp32 pattern.
