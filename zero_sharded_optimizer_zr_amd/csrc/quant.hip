@@ -33,9 +33,9 @@ constexpr int kTileChunks = 4;
 constexpr int kTile = kChunk * kTileChunks;
 constexpr int kRow = 16 * kLaneVec;  // elements of one DPP row of 16 lanes
 
-// Blocks whose scale is 0 or at least kFastMinScale take the corrected
-// reciprocal quotient of quantize8; tinier scales (where its FMA remainder can
-// underflow) divide exactly.  As bit patterns of non-negative floats.
+// Tiles whose block scales are all 0 or at least 2^-100 take quantize_fast;
+// a tile with a tinier scale (where its FMA remainder can underflow) divides
+// exactly.  As the bit pattern of a non-negative float.
 constexpr uint32_t kFastMinScaleBits = 0x0d800000u;  // 2^-100
 
 // Wave identity as a scalar: threadIdx.x >> 6 is the same in every lane.
