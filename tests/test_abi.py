@@ -399,3 +399,37 @@ def test_unpack_int8_validation():
     assert call(lay.handle, q, sc, 256, 0, 16, views=over_q) == zr.ZR_EINVAL
     over_s = _views((A, 0, 10), (sc - 4, 0, 6), (None, 0, 0))
     assert call(lay.handle, q, sc, 256, 0, 16, views=over_s) == zr.ZR_EINVAL
+
+
+def test_binding_rejects_short_tensors():
+    """Every wrapper checks that each tensor holds the count it is asked to
+    process before anything reaches the library (no GPU is touched)."""
+    i16 = lambda n: torch.zeros(n, dtype=torch.int16)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    hp = dict(lr=5e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
+    lay = zr.zr_layout_create([300_000, 200_000], 4)
+    cases = [
+        lambda: zr.zr_pack(lay, [i16(300_000), i16(200_000)], i16(99), 0, 100),
+        lambda: zr.zr_unpack(lay, i16(99), 0, 100, [i16(300_000), i16(200_000)]),
+        lambda: zr.zr_reduce_slice([i16(100), i16(99)], i16(100)),
+        lambda: zr.zr_adamw_step(i16(99), f32(100), f32(100), f32(100), i16(100), **hp),
+        lambda: zr.zr_adamw_step(i16(100), f32(100), f32(99), f32(100), None, **hp),
+        lambda: zr.zr_adamw_step(i16(100), f32(100), f32(100), f32(100), i16(99), **hp),
+        lambda: zr.zr_reduce_adamw_step([i16(100), i16(99)], f32(100), f32(100), f32(100), None, **hp),
+        lambda: zr.zr_reduce_adamw_step([i16(100)], f32(100), f32(100), f32(100), None, i16(99), **hp),
+        lambda: zr.zr_reduce_slice_f16([i16(99)], i16(100)),
+        lambda: zr.zr_check_finite_f16(i16(99), torch.zeros(4, dtype=torch.int32), numel=100),
+        lambda: zr.zr_adamw_step_f16(i16(99), f32(100), f32(100), f32(100), None,
+                                     torch.zeros(4, dtype=torch.int32), **hp),
+        lambda: zr.zr_quantize_int8(i16(99), torch.zeros(100, dtype=torch.int8), f32(1), block=256, numel=100),
+        lambda: zr.zr_dequantize_int8(torch.zeros(100, dtype=torch.int8), f32(1), i16(99), block=256, numel=100),
+        lambda: zr.zr_unpack_int8(lay, torch.zeros(999, dtype=torch.int8), f32(100), 0, 1000,
+                                  [i16(300_000), i16(200_000)], block=256),
+        # [124_900, 125_100) crosses the first shard edge: 2 blocks of 256 on each side -> 3 scales
+        lambda: zr.zr_unpack_int8(lay, torch.zeros(200, dtype=torch.int8), f32(2), 124_900, 125_100,
+                                  [i16(300_000), i16(200_000)], block=256),
+        lambda: zr.zr_host_adamw_step(i16(100), f32(100), f32(100), f32(99), None, **hp),
+    ]
+    for k, call in enumerate(cases):
+        with pytest.raises(ValueError):
+            call()

@@ -133,6 +133,15 @@ def _ptr(t: Optional[torch.Tensor], size: int, name: str) -> Optional[int]:
     return t.data_ptr() or None
 
 
+def _need(n: int, **tensors):
+    """Every given tensor (None skipped) must hold at least n elements: the
+    library trusts the counts it is given, so a short tensor would mean an
+    access past its end on the device."""
+    for name, t in tensors.items():
+        if t is not None and t.numel() < n:
+            raise ValueError(f"{name} holds {t.numel()} elements, {n} needed")
+
+
 # ---------------------------------------------------------------- layout ----
 
 class Layout:
@@ -223,6 +232,7 @@ def zr_pack(layout: Layout, views: Sequence[ViewArg], flat: torch.Tensor, begin:
             stream=None) -> None:
     """flat (holding flat elements [begin, end)) <- per-tensor views; padding zeroed.
     views[t] is None, a tensor holding all of tensor t, or (tensor, first)."""
+    _need(int(end) - int(begin), flat=flat)
     _check(_lib.zr_pack(layout.handle, _views(layout, views), len(views), _ptr(flat, 2, "flat"),
                         int(begin), int(end), _stream(stream)))
 
@@ -230,6 +240,7 @@ def zr_pack(layout: Layout, views: Sequence[ViewArg], flat: torch.Tensor, begin:
 def zr_unpack(layout: Layout, flat: torch.Tensor, begin: int, end: int, views: Sequence[ViewArg],
               stream=None) -> None:
     """per-tensor views <- flat elements [begin, end)."""
+    _need(int(end) - int(begin), flat=flat)
     _check(_lib.zr_unpack(layout.handle, _ptr(flat, 2, "flat"), int(begin), int(end),
                           _views(layout, views), len(views), _stream(stream)))
 
@@ -242,6 +253,7 @@ def zr_reduce_slice(contribs: Sequence[torch.Tensor], out: torch.Tensor, numel: 
     n = len(contribs)
     table = (ctypes.c_void_p * max(1, n))(*[_ptr(c, 2, f"contribs[{k}]") for k, c in enumerate(contribs)])
     numel = out.numel() if numel is None else int(numel)
+    _need(numel, out=out, **{f"contribs[{k}]": c for k, c in enumerate(contribs)})
     _check(_lib.zr_reduce_slice(table, n, numel, _ptr(out, 2, "out"), _stream(stream)))
 
 
@@ -254,6 +266,7 @@ def zr_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tenso
     hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
                   int(step))
     numel = master.numel() if numel is None else int(numel)
+    _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
     _check(_lib.zr_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                               _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
                               ctypes.byref(hp), _stream(stream)))
@@ -271,6 +284,8 @@ def zr_reduce_adamw_step(contribs: Sequence[torch.Tensor], master: torch.Tensor,
     hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
                   int(step))
     numel = master.numel() if numel is None else int(numel)
+    _need(numel, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out, grad_out=grad_out,
+          **{f"contribs[{k}]": c for k, c in enumerate(contribs)})
     _check(_lib.zr_reduce_adamw_step(table, n, _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                                      _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"),
                                      _ptr(grad_out, 2, "grad_out"), numel, ctypes.byref(hp), _stream(stream)))
@@ -303,11 +318,13 @@ def zr_reduce_slice_f16(contribs: Sequence[torch.Tensor], out: torch.Tensor, ls:
     n = len(contribs)
     table = (ctypes.c_void_p * max(1, n))(*[_ptr(c, 2, f"contribs[{k}]") for k, c in enumerate(contribs)])
     numel = out.numel() if numel is None else int(numel)
+    _need(numel, out=out, **{f"contribs[{k}]": c for k, c in enumerate(contribs)})
     _check(_lib.zr_reduce_slice_f16(table, n, numel, _ptr(out, 2, "out"), _ls(ls), _stream(stream)))
 
 
 def zr_check_finite_f16(grad: torch.Tensor, ls: torch.Tensor, numel: Optional[int] = None, stream=None) -> None:
     numel = grad.numel() if numel is None else int(numel)
+    _need(numel, grad=grad)
     _check(_lib.zr_check_finite_f16(_ptr(grad, 2, "grad"), numel, _ls(ls), _stream(stream)))
 
 
@@ -320,6 +337,7 @@ def zr_adamw_step_f16(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.T
     hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
                   int(step))
     numel = master.numel() if numel is None else int(numel)
+    _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
     _check(_lib.zr_adamw_step_f16(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                                   _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
                                   ctypes.byref(hp), _ls(ls), _stream(stream)))
@@ -344,6 +362,7 @@ def zr_quantize_int8(src: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, b
     """Per block of `block` elements of bf16 src: scales[b] = amax / 127 and
     q[i] = rint(src[i] / scales[b]) clamped to +-127."""
     numel = src.numel() if numel is None else int(numel)
+    _need(numel, src=src)
     _int8_sizes(numel, int(block), q, scales)
     _check(_lib.zr_quantize_int8(_ptr(src, 2, "src"), numel, int(block), _ptr(q, 1, "q"),
                                  _ptr(scales, 4, "scales"), _stream(stream)))
@@ -353,6 +372,7 @@ def zr_dequantize_int8(q: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor,
                        numel: Optional[int] = None, stream=None) -> None:
     """dst[i] = bf16(q[i] * scales[i // block])."""
     numel = dst.numel() if numel is None else int(numel)
+    _need(numel, dst=dst)
     _int8_sizes(numel, int(block), q, scales)
     _check(_lib.zr_dequantize_int8(_ptr(q, 1, "q"), _ptr(scales, 4, "scales"), numel, int(block),
                                    _ptr(dst, 2, "dst"), _stream(stream)))
@@ -363,8 +383,12 @@ def zr_unpack_int8(layout: Layout, q: torch.Tensor, scales: torch.Tensor, begin:
     """Per-tensor views <- bf16(code * scale) for flat elements [begin, end) of
     a quantized AllGather (per-shard blocks); q[k] is the code of element
     begin + k and scales[0] the scale of the block holding element begin."""
-    if q.numel() < end - begin:
-        raise ValueError(f"q holds {q.numel()} codes, {end - begin} needed")
+    _need(int(end) - int(begin), q=q)
+    if end > begin and int(block) > 0:
+        S = zr_layout_query(layout)["shard"]
+        per_rank = -(-S // int(block))
+        g = lambda i: (i // S) * per_rank + (i % S) // int(block)
+        _need(g(int(end) - 1) - g(int(begin)) + 1, scales=scales)
     _check(_lib.zr_unpack_int8(layout.handle, _ptr(q, 1, "q"), _ptr(scales, 4, "scales"), int(block), int(begin),
                                int(end), _views(layout, views), len(views), _stream(stream)))
 
@@ -395,6 +419,7 @@ def zr_host_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.
     hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
                   int(step))
     numel = master.numel() if numel is None else int(numel)
+    _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
     _check(_lib.zr_host_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                                    _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
                                    ctypes.byref(hp), int(threads)))
@@ -421,6 +446,7 @@ def zr_offload_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: tor
     hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
                   int(step))
     numel = master.numel() if numel is None else int(numel)
+    _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
     _check(_lib.zr_offload_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
                                       _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
                                       ctypes.byref(hp), _ptr(staging, 1, "staging"), staging.numel(), int(threads),
