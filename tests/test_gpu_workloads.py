@@ -347,3 +347,74 @@ def test_fp16_loss_scaled_step_full_size():
     assert torch.equal(psnap.view(torch.int16), param.view(torch.int16))
     r = ls.cpu()
     assert float(r.view(torch.float32)[0]) == 32768.0 and int(r[3]) == 1
+
+
+def test_next_kernels_beyond_2_pow_31_elements():
+    """64-bit indexing of the fused reduce + AdamW, the fp16 mean and AdamW,
+    the int8 codec and the dequantize-on-unpack over more than 2^31 elements,
+    each checked on sampled elements (or sampled blocks) against the oracle."""
+    dev = device()
+    n = (1 << 31) + 13
+    w = FLAT_7B
+    idx = sample_idx(n, 37, dev)
+    # fused reduce + AdamW, two contributions
+    say("fused / fp16 / int8 over", n, "elements")
+    contribs = [synth.normal_bf16(n, 1e-3, 95 + k, dev) for k in range(2)]
+    st = synth.shard_state(w, n, device=dev)
+    before = [take32(st[k], idx) for k in ("master", "exp_avg", "exp_avg_sq")]
+    param = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    zr.zr_reduce_adamw_step(contribs, st["master"], st["exp_avg"], st["exp_avg_sq"], param, step=10, **w.hparams)
+    torch.cuda.synchronize()
+    o_grad = oracle.reduce([take16(c, idx) for c in contribs])
+    o_param = np.zeros(idx.numel(), np.uint16)
+    oracle.adamw(o_grad, *before, o_param, step=10, **w.hparams)
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
+        assert_fp32_close(take32(st[k], idx), want, f"fused beyond 2^31 {name}")
+    assert_bf16_within_1ulp(take16(param, idx), o_param, "fused beyond 2^31 param")
+    del contribs
+    torch.cuda.empty_cache()
+    # fp16 mean with the overflow flag, then the loss-scaled AdamW
+    scale = 2.0 ** 16
+    c16 = [(synth.normal_f32(n, 1e-3 * scale, 97 + k, dev)).to(torch.float16) for k in range(2)]
+    g16 = torch.empty(n, dtype=torch.float16, device=dev)
+    ls = zr.loss_scale_record(dev)
+    zr.zr_loss_scale_init(ls, scale)
+    zr.zr_reduce_slice_f16(c16, g16, ls)
+    before = [take32(st[k], idx) for k in ("master", "exp_avg", "exp_avg_sq")]
+    p16 = torch.empty(n, dtype=torch.float16, device=dev)
+    zr.zr_adamw_step_f16(g16, st["master"], st["exp_avg"], st["exp_avg_sq"], p16, ls, step=11, **w.hparams)
+    torch.cuda.synchronize()
+    assert int(ls.cpu()[2]) == 0
+    o_g16 = oracle.reduce_f16([take16(c, idx) for c in c16])
+    assert_bits_equal(take16(g16, idx), o_g16, "fp16 mean beyond 2^31")
+    o_p16 = np.zeros(idx.numel(), np.uint16)
+    oracle.adamw_f16(o_g16, *before, o_p16, step=11, loss_scale=scale, **w.hparams)
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
+        assert_fp32_close(take32(st[k], idx), want, f"fp16 adamw beyond 2^31 {name}")
+    del c16, g16, p16, st
+    torch.cuda.empty_cache()
+    # int8 codec over the bf16 parameters, sampled blocks
+    block = 2048
+    nb = -(-n // block)
+    q = torch.empty(n, dtype=torch.int8, device=dev)
+    sc = torch.empty(nb, dtype=torch.float32, device=dev)
+    back = torch.empty(n, dtype=torch.int16, device=dev)
+    zr.zr_quantize_int8(param, q, sc, block=block)
+    zr.zr_dequantize_int8(q, sc, back, block=block)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(2)
+    for b in np.unique(np.concatenate([rng.integers(0, nb, 300), [nb // 2, nb - 2, nb - 1]])):
+        lo, hi = int(b) * block, min(n, (int(b) + 1) * block)
+        rq, rs = oracle.quantize_int8(param.view(torch.int16)[lo:hi].cpu().numpy().view(np.uint16).copy(), block)
+        assert_bits_equal(sc[int(b):int(b) + 1].cpu().numpy(), rs, f"scale of block {b}")
+        assert_bits_equal(q[lo:hi].cpu().numpy(), rq, f"codes of block {b}")
+        assert_bits_equal(back[lo:hi].cpu().numpy().view(np.uint16), oracle.dequantize_int8(rq, rs, block),
+                          f"rebuilt block {b}")
+    # the same codes as one rank's gathered buffer, rebuilt into a tensor view
+    glay = zr.zr_layout_create([n], 1, 0)
+    out = torch.empty(n, dtype=torch.int16, device=dev)
+    zr.zr_unpack_int8(glay, q, sc, 0, n, [out], block=block)
+    torch.cuda.synchronize()
+    assert torch.equal(out, back)
+    del q, sc, back, out, param
+    torch.cuda.empty_cache()
