@@ -275,6 +275,10 @@ def main():
                        "step_algorithmic_bytes": sum(fbytes.values()), "kernels": fkernels},
     }
 
+    # the same four calls recorded once as a graph, replayed with this step's AdamW scalars
+    result["graph_step"] = graph_leg(lay, own_grad, contribs, grad, master, m, v, flat_param, params, b, e, S, hp,
+                                     t_step, args)
+
     if not args.no_extra_paths:
         result["fp16_path"] = fp16_leg(w, lay, b, e, S, frags, params, st, hp, t_step, args, stream)
         result["qwz_gather"] = qwz_leg(w, lay, info, b, S, flat_param, args, stream)
@@ -284,6 +288,41 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, lay, frags, b, min(args.cpu_sample, S), own_grad, contribs,
                                               st, hp, t_step, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def graph_leg(lay, own_grad, contribs, grad, master, m, v, flat_param, params, b, e, S, hp, t_step, args):
+    """The step's four calls recorded once on a side stream (zr_graph_*) and
+    replayed: zr_graph_set_adamw then zr_graph_launch per step, timed like the
+    eager step (wall clock over the timed steps, synchronised on both sides)."""
+    import torch
+
+    import zero_sharded_optimizer_zr_amd as zr
+
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        zr.zr_graph_capture_begin()
+        zr.zr_pack(lay, own_grad, contribs[0], b, e)
+        zr.zr_reduce_slice(contribs, grad)
+        zr.zr_adamw_step(grad, master, m, v, flat_param, step=t_step, **hp)
+        zr.zr_unpack(lay, flat_param, b, e, params)
+        g = zr.zr_graph_capture_end()
+    kernels, _ = zr.zr_graph_info(g)
+
+    def step():
+        zr.zr_graph_set_adamw(g, step=t_step, **hp)
+        zr.zr_graph_launch(g, side)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    zr.zr_graph_destroy(g)
+    return {"ms_per_step": round(ms, 4), "value": S / (ms * 1e-3), "unit": "elements/s", "kernel_nodes": kernels}
 
 
 def fp16_leg(w, lay, b, e, S, frags, params, st, hp, t_step, args, stream):

@@ -434,6 +434,51 @@ ZR_API zr_status zr_offload_adamw_step(const void *grad, float *master, float *e
                                        void *param_out, int64_t numel, const zr_adamw_hparams *hp, void *staging,
                                        int64_t staging_bytes, int32_t threads, void *stream);
 
+/* ------------------------------------------------------ captured steps ---- */
+
+/*
+ * A sequence of the calls above, recorded once on a stream as a HIP graph and
+ * replayed as one launch (an execution facility: the operations are those of
+ * the recorded calls).  A training loop repeats the same calls on the same
+ * buffers every step; on small shards the launches dominate the step.
+ *
+ *   zr_graph_capture_begin(s);  ...calls on stream s...;  zr_graph_capture_end(s, &g);
+ *   for each step: zr_graph_set_adamw(g, &hp_t); zr_graph_launch(g, s);
+ *
+ * Buffers, sizes, layouts and the fp16 loss-scale record are fixed at
+ * capture; the AdamW hyper-parameters (step t, lr, ...) of every recorded
+ * AdamW-family call (zr_adamw_step, zr_reduce_adamw_step, zr_adamw_step_f16)
+ * are replaced by zr_graph_set_adamw, which affects the following launches
+ * (until then the captured values apply).  A replay gives the same bits as
+ * the eager calls.  The calls are validated at capture time, as usual, and
+ * enqueue nothing then.  zr_offload_adamw_step synchronises with the host and
+ * cannot be recorded.  Launching the same graph on two streams at once races.
+ */
+typedef struct zr_graph zr_graph;
+
+/* Starts recording on `stream` (not the null stream; thread-local capture
+ * mode).  Errors: ZR_EINVAL, ZR_EHIP. */
+ZR_API zr_status zr_graph_capture_begin(void *stream);
+
+/* Ends the recording and instantiates it; *out owns it (zr_graph_destroy).
+ * Errors: ZR_EINVAL (NULL argument, nothing recorded), ZR_ENOMEM, ZR_EHIP. */
+ZR_API zr_status zr_graph_capture_end(void *stream, zr_graph **out);
+
+/* Kernel nodes recorded, and how many of them take AdamW hyper-parameters.
+ * Either output may be NULL.  Errors: ZR_EINVAL. */
+ZR_API zr_status zr_graph_info(const zr_graph *g, int32_t *kernels, int32_t *adamw_nodes);
+
+/* Hyper-parameters for every AdamW-family node of the following launches
+ * (validated like zr_adamw_step).  Errors: ZR_EINVAL, ZR_EHIP. */
+ZR_API zr_status zr_graph_set_adamw(zr_graph *g, const zr_adamw_hparams *hp);
+
+/* Replays the graph on `stream`.  Errors: ZR_EINVAL, ZR_EHIP. */
+ZR_API zr_status zr_graph_launch(zr_graph *g, void *stream);
+
+/* Releases the graph; NULL is ignored.  Wait for its launches to finish
+ * first. */
+ZR_API void zr_graph_destroy(zr_graph *g);
+
 /* ------------------------------------------------------------- misc ------ */
 
 /* Message for the last failing call on this thread ("" if none). */

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 31
     lib = ctypes.CDLL(zr.LIBRARY)
     for name in names:
         assert hasattr(lib, name), name
@@ -433,3 +433,14 @@ def test_binding_rejects_short_tensors():
     for k, call in enumerate(cases):
         with pytest.raises(ValueError):
             call()
+
+
+def test_graph_validation():
+    L = zr._lib
+    hp = _hp()
+    assert L.zr_graph_capture_begin(None) == zr.ZR_EINVAL
+    assert L.zr_graph_capture_end(None, None) == zr.ZR_EINVAL
+    assert L.zr_graph_info(None, None, None) == zr.ZR_EINVAL
+    assert L.zr_graph_set_adamw(None, ctypes.byref(hp)) == zr.ZR_EINVAL
+    assert L.zr_graph_launch(None, None) == zr.ZR_EINVAL
+    L.zr_graph_destroy(None)

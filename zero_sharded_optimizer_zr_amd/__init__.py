@@ -89,6 +89,12 @@ _SIGS = {
     "zr_host_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _I32], _I32),
     "zr_host_simd": ([], ctypes.c_char_p),
     "zr_offload_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I32, _P], _I32),
+    "zr_graph_capture_begin": ([_P], _I32),
+    "zr_graph_capture_end": ([_P, _P], _I32),
+    "zr_graph_info": ([_P, _P, _P], _I32),
+    "zr_graph_set_adamw": ([_P, _P], _I32),
+    "zr_graph_launch": ([_P, _P], _I32),
+    "zr_graph_destroy": ([_P], None),
     "zr_last_error": ([], ctypes.c_char_p),
     "zr_abi_version": ([], _I32),
 }
@@ -451,4 +457,59 @@ def zr_offload_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: tor
                                       _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
                                       ctypes.byref(hp), _ptr(staging, 1, "staging"), staging.numel(), int(threads),
                                       _stream(stream)))
+
+
+# ---------------------------------------------------------- captured steps ----
+
+class Graph:
+    """Owns a zr_graph (released on garbage collection)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value and _lib is not None:
+            _lib.zr_graph_destroy(self._h)
+            self._h = ctypes.c_void_p(None)
+
+
+def zr_graph_capture_begin(stream=None) -> None:
+    """Start recording library calls on `stream` (default: torch's current
+    stream, which must not be the default stream)."""
+    _check(_lib.zr_graph_capture_begin(_stream(stream)))
+
+
+def zr_graph_capture_end(stream=None) -> Graph:
+    h = ctypes.c_void_p()
+    _check(_lib.zr_graph_capture_end(_stream(stream), ctypes.byref(h)))
+    return Graph(h.value)
+
+
+def zr_graph_info(g: Graph) -> Tuple[int, int]:
+    """(kernel nodes, AdamW-family nodes) of a captured graph."""
+    k, a = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.zr_graph_info(g.handle, ctypes.byref(k), ctypes.byref(a)))
+    return k.value, a.value
+
+
+def zr_graph_set_adamw(g: Graph, *, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                       step: int, grad_scale: float = 1.0) -> None:
+    """AdamW hyper-parameters for the graph's following launches."""
+    hp = _HParams(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay), float(grad_scale),
+                  int(step))
+    _check(_lib.zr_graph_set_adamw(g.handle, ctypes.byref(hp)))
+
+
+def zr_graph_launch(g: Graph, stream=None) -> None:
+    _check(_lib.zr_graph_launch(g.handle, _stream(stream)))
+
+
+def zr_graph_destroy(g: Graph) -> None:
+    if g._h.value:
+        _lib.zr_graph_destroy(g._h)
+        g._h = ctypes.c_void_p(None)
 

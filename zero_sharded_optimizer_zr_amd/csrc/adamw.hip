@@ -96,6 +96,14 @@ __global__ __launch_bounds__(kBlock) void adamw_scalar_kernel(const uint16_t *gr
         adamw_one(grad, master, m, v, param, j, s);
 }
 
+int adamw_scalar_slots(ScalarSlot *out)
+{
+    out[0] = slot_of(adamw_vec_kernel<true>);
+    out[1] = slot_of(adamw_vec_kernel<false>);
+    out[2] = slot_of(adamw_scalar_kernel);
+    return 3;
+}
+
 }  // namespace zr
 
 using namespace zr;

@@ -292,6 +292,14 @@ inline zr_status check_ls(const char *who, const void *ls)
     return ZR_OK;
 }
 
+int fp16_scalar_slots(ScalarSlot *out)
+{
+    out[0] = slot_of(adamw_f16_vec_kernel<true>);
+    out[1] = slot_of(adamw_f16_vec_kernel<false>);
+    out[2] = slot_of(adamw_f16_scalar_kernel);
+    return 3;
+}
+
 }  // namespace zr
 
 using namespace zr;

@@ -174,6 +174,25 @@ static zr_status fused_launch(const void *const *contribs, int32_t n, float *mas
     return fused_vec_launch<MaxN, false, false>(c, n, master, m, v, param, gout, numel, head, groups, d, s, st);
 }
 
+template <int MaxN>
+static int fused_slots_for(ScalarSlot *out)
+{
+    out[0] = slot_of(fused_vec_kernel<MaxN, true, true>);
+    out[1] = slot_of(fused_vec_kernel<MaxN, true, false>);
+    out[2] = slot_of(fused_vec_kernel<MaxN, false, true>);
+    out[3] = slot_of(fused_vec_kernel<MaxN, false, false>);
+    out[4] = slot_of(fused_scalar_kernel<MaxN>);
+    return 5;
+}
+
+int fused_scalar_slots(ScalarSlot *out)
+{
+    int k = fused_slots_for<8>(out);
+    k += fused_slots_for<64>(out + k);
+    k += fused_slots_for<kMaxContribs>(out + k);
+    return k;
+}
+
 }  // namespace zr
 
 using namespace zr;

@@ -5,6 +5,7 @@
 #pragma once
 
 #include <cmath>
+#include <type_traits>
 
 #include "zr_device.hpp"
 #include "zr_internal.hpp"
@@ -114,6 +115,41 @@ inline AdamWScalars adamw_scalars(const zr_adamw_hparams &hp)
     s.grad_scale = (float)hp.grad_scale;
     return s;
 }
+
+// ------------------------------------------------- graph parameter slots --
+
+// A kernel that takes the per-step AdamW scalars by value, as captured graphs
+// see it: its host-side address, its argument count and the position of the
+// AdamWScalars argument (deduced from the signature at compile time).
+struct ScalarSlot {
+    const void *func;
+    int nargs;
+    int index;
+};
+
+template <typename T, typename... A>
+constexpr int arg_index()
+{
+    constexpr bool match[] = {std::is_same<T, A>::value..., false};
+    for (int i = 0; i < (int)sizeof...(A); ++i)
+        if (match[i])
+            return i;
+    return -1;
+}
+
+template <typename... A>
+ScalarSlot slot_of(void (*kernel)(A...))
+{
+    static_assert(arg_index<AdamWScalars, A...>() >= 0, "kernel takes no AdamWScalars");
+    return ScalarSlot{reinterpret_cast<const void *>(kernel), (int)sizeof...(A), arg_index<AdamWScalars, A...>()};
+}
+
+// The AdamW-family kernels of each translation unit (adamw.hip, fused.hip,
+// fp16.hip); each writes its slots to `out` and returns how many.
+int adamw_scalar_slots(ScalarSlot *out);
+int fused_scalar_slots(ScalarSlot *out);
+int fp16_scalar_slots(ScalarSlot *out);
+constexpr int kMaxScalarSlots = 64;
 
 // No two of `count` buffers (pointer, byte length) may overlap; NULL entries
 // are skipped.  Returns the index pair of the first overlap through a, b.
