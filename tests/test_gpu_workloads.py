@@ -418,3 +418,69 @@ def test_next_kernels_beyond_2_pow_31_elements():
     assert torch.equal(out, back)
     del q, sc, back, out, param
     torch.cuda.empty_cache()
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("w", [LLAMA_7B, GPT_7P5B, FLAT_1T], ids=lambda w: w.name)
+def test_next_paths_on_full_size_shards(w):
+    """The fused reduce + AdamW (with its bf16 mean output), the fp16 mean and
+    loss-scaled AdamW, and the int8 codes of the updated parameters, on the
+    rank's full shard of each workload, sampled against the oracle."""
+    dev = device()
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    b, e = zr.zr_layout_rank_range(lay, w.rank)
+    n = e - b
+    t = w.steps[0]
+    idx = sample_idx(n, 77 + w.seed, dev)
+    say(w.name, "next paths over", n, "elements,", w.n_contrib, "contributions")
+    # fused reduce + AdamW
+    contribs = synth.contributions(w, n, device=dev, salt=5)
+    st = synth.shard_state(w, n, device=dev, salt=5)
+    before = [take32(st[k], idx) for k in ("master", "exp_avg", "exp_avg_sq")]
+    param = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    gout = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    zr.zr_reduce_adamw_step(contribs, st["master"], st["exp_avg"], st["exp_avg_sq"], param, gout, step=t,
+                            **w.hparams)
+    torch.cuda.synchronize()
+    o_grad = oracle.reduce([take16(c, idx) for c in contribs])
+    assert_bits_equal(take16(gout, idx), o_grad, f"{w.name} fused mean")
+    o_param = np.zeros(idx.numel(), np.uint16)
+    oracle.adamw(o_grad, *before, o_param, step=t, **w.hparams)
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
+        assert_fp32_close(take32(st[k], idx), want, f"{w.name} fused {name}")
+    assert_bf16_within_1ulp(take16(param, idx), o_param, f"{w.name} fused param")
+    del contribs, gout
+    torch.cuda.empty_cache()
+    # fp16 mean and loss-scaled AdamW
+    scale = 2.0 ** 16
+    c16 = [synth.normal_f32(n, w.grad_std * scale, 300 + k, dev).to(torch.float16) for k in range(w.n_contrib)]
+    g16 = torch.empty(n, dtype=torch.float16, device=dev)
+    ls = zr.loss_scale_record(dev)
+    zr.zr_loss_scale_init(ls, scale)
+    zr.zr_reduce_slice_f16(c16, g16, ls)
+    before = [take32(st[k], idx) for k in ("master", "exp_avg", "exp_avg_sq")]
+    zr.zr_adamw_step_f16(g16, st["master"], st["exp_avg"], st["exp_avg_sq"], None, ls, step=t + 1, **w.hparams)
+    torch.cuda.synchronize()
+    assert int(ls.cpu()[2]) == 0
+    o_g16 = oracle.reduce_f16([take16(c, idx) for c in c16])
+    assert_bits_equal(take16(g16, idx), o_g16, f"{w.name} fp16 mean")
+    oracle.adamw_f16(o_g16, *before, None, step=t + 1, loss_scale=scale, **w.hparams)
+    for name, k, want in zip(("master", "m", "v"), ("master", "exp_avg", "exp_avg_sq"), before):
+        assert_fp32_close(take32(st[k], idx), want, f"{w.name} fp16 {name}")
+    del c16, g16, st
+    torch.cuda.empty_cache()
+    # int8 codes of the updated parameters (the rank's contribution to the quantized gather)
+    block = 512
+    nb = -(-n // block)
+    q = torch.empty(n, dtype=torch.int8, device=dev)
+    sc = torch.empty(nb, dtype=torch.float32, device=dev)
+    zr.zr_quantize_int8(param, q, sc, block=block)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed)
+    for blk in np.unique(np.concatenate([rng.integers(0, nb, 200), [0, nb - 1]])):
+        lo, hi = int(blk) * block, min(n, (int(blk) + 1) * block)
+        rq, rs = oracle.quantize_int8(param.view(torch.int16)[lo:hi].cpu().numpy().view(np.uint16).copy(), block)
+        assert_bits_equal(sc[int(blk):int(blk) + 1].cpu().numpy(), rs, f"{w.name} scale {blk}")
+        assert_bits_equal(q[lo:hi].cpu().numpy(), rq, f"{w.name} codes {blk}")
+    del q, sc, param
+    torch.cuda.empty_cache()
