@@ -423,10 +423,11 @@ ZR_API const char *zr_host_simd(void);
  * bf16 [numel], or NULL for no copy).  staging is caller-owned pinned host
  * memory (hipHostMalloc), 64-byte aligned, of staging_bytes >=
  * ZR_OFFLOAD_MIN_STAGING; the shard goes through it in chunks of
- * staging_bytes / 8 elements (rounded down to a multiple of 64), so that the
- * copy of one chunk overlaps the host update of the next.  Copies are enqueued
- * on `stream`, after the work already there (e.g. the reduce that produced
- * grad).  The call is synchronous: it returns when the states are updated and
+ * staging_bytes / 12 elements (rounded down to a multiple of 64; three chunks
+ * in flight), so that the copies of neighbouring chunks overlap the host update
+ * of one.  Gradient copies are enqueued on `stream`, after the work already
+ * there (e.g. the reduce that produced grad); parameter copies go on a stream
+ * the library keeps per device.  The call is synchronous: it returns when the states are updated and
  * every parameter has reached the device (or, on an error, when the copies it
  * enqueued have finished).  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
  */

@@ -10,13 +10,14 @@
 // is rounded to nearest even with integer arithmetic, NaN kept quiet.  Work is
 // split over a persistent pool of host threads in contiguous ranges.
 //
-// Offload pipeline: the shard is processed in chunks that fit half of the
+// Offload pipeline: the shard is processed in chunks that fit a third of the
 // caller's pinned staging buffer (a bf16 gradient slot and a bf16 parameter
-// slot per half).  Copies are enqueued on the caller's stream, so the first
-// gradient copy follows whatever produced the gradient; while the host updates
-// chunk i, the parameter copy of chunk i - 1 and the gradient copy of chunk
-// i + 1 run on the copy engine.  The call returns when every parameter has
-// reached the device.
+// slot per third).  Gradient copies go on the caller's stream, so the first one
+// follows whatever produced the gradient; parameter copies go on a stream of
+// their own, so both directions of PCIe are busy at once.  While the host
+// updates chunk i, the gradients of chunks i+1 and i+2 come down and the
+// parameters of chunks i-1 and i-2 go up.  The call returns when every
+// parameter has reached the device.
 //
 // Sources (web pages on DeepSpeed ZeRO-3): ZeRO tutorial (cnhsyj.com) 3.2
 // (cpu_offload moves optimizer states, gradients and even parameters to CPU
@@ -333,17 +334,29 @@ zr_status check_host_buffers(const char *who, const void *grad, const float *mas
     return ZR_OK;
 }
 
-// Waits for a HIP event; returns ZR_EHIP with the message on failure.
+// Waits for a HIP event by polling (a copy of one chunk takes a fraction of a
+// millisecond, and a blocking wait's wake-up latency is a sizeable part of
+// that); returns ZR_EHIP with the message on failure.
 zr_status wait_event(hipEvent_t e, const char *who)
 {
-    hipError_t err = hipEventSynchronize(e);
-    if (err != hipSuccess)
-        return fail(ZR_EHIP, "%s: %s", who, hipGetErrorString(err));
-    return ZR_OK;
+    for (;;) {
+        const hipError_t err = hipEventQuery(e);
+        if (err == hipSuccess)
+            return ZR_OK;
+        if (err != hipErrorNotReady)
+            return fail(ZR_EHIP, "%s: %s", who, hipGetErrorString(err));
+        for (int k = 0; k < 64; ++k)
+            _mm_pause();
+    }
 }
 
+// Staging slots in flight: chunk i uses slot i % kSlots, so while the host
+// updates chunk i, the gradients of chunks i+1 and i+2 can be coming down and
+// the parameters of chunks i-1 and i-2 going up.
+constexpr int kSlots = 3;
+
 struct Events {
-    hipEvent_t e[4] = {nullptr, nullptr, nullptr, nullptr};
+    hipEvent_t e[2 * kSlots] = {};  // gradient copy done [0, kSlots), parameter copy done [kSlots, 2 kSlots)
     ~Events()
     {
         for (auto x : e)
@@ -351,6 +364,27 @@ struct Events {
                 (void)hipEventDestroy(x);
     }
 };
+
+// The stream of the parameter copies, one per device, made on first use (the
+// gradient copies go on the caller's stream, after the work that produced the
+// gradient; on a stream of their own the two directions of PCIe run at once).
+zr_status upload_stream(hipStream_t *out, const char *who)
+{
+    static std::mutex mu;
+    static std::vector<hipStream_t> streams;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(ZR_EHIP, "%s: hipGetDevice failed", who);
+    std::lock_guard<std::mutex> lk(mu);
+    if ((int)streams.size() <= dev)
+        streams.resize(dev + 1, nullptr);
+    if (!streams[dev] && hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking) != hipSuccess) {
+        streams[dev] = nullptr;
+        return fail(ZR_EHIP, "%s: hipStreamCreateWithFlags failed", who);
+    }
+    *out = streams[dev];
+    return ZR_OK;
+}
 
 }  // namespace
 }  // namespace zr
@@ -409,28 +443,31 @@ extern "C" zr_status zr_offload_adamw_step(const void *grad, float *master, floa
         return ZR_OK;
 
     const AdamWScalars s = adamw_scalars(*hp);
-    hipStream_t str = static_cast<hipStream_t>(stream);
-    // chunk: elements per half of the staging buffer (a gradient and a parameter slot)
-    const int64_t chunk = std::min<int64_t>(numel, staging_bytes / 8 / 64 * 64);
+    hipStream_t str = static_cast<hipStream_t>(stream), up = nullptr;
+    if (param_out && (st = upload_stream(&up, who)) != ZR_OK)
+        return st;
+    // chunk: elements per slot pair (a gradient and a parameter slot)
+    const int64_t chunk = std::min<int64_t>(numel, staging_bytes / (4 * kSlots) / 64 * 64);
     const int64_t nchunks = (numel + chunk - 1) / chunk;
-    uint16_t *gslot[2], *pslot[2];
-    for (int k = 0; k < 2; ++k) {
+    uint16_t *gslot[kSlots], *pslot[kSlots];
+    for (int k = 0; k < kSlots; ++k) {
         gslot[k] = static_cast<uint16_t *>(staging) + (2 * k) * chunk;
         pslot[k] = static_cast<uint16_t *>(staging) + (2 * k + 1) * chunk;
     }
     const uint16_t *g = static_cast<const uint16_t *>(grad);
     uint16_t *pd = static_cast<uint16_t *>(param_out);
 
-    Events ev;  // d2h[0], d2h[1], h2d[0], h2d[1]
+    Events ev;
     for (auto &e : ev.e)
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess)
             return fail(ZR_EHIP, "%s: hipEventCreateWithFlags failed", who);
+    hipEvent_t *fetched = ev.e, *sent = ev.e + kSlots;
 
     auto len_of = [&](int64_t i) { return std::min(chunk, numel - i * chunk); };
-    auto fetch = [&](int64_t i) -> zr_status {  // gradient chunk i -> slot i % 2
-        const int k = (int)(i & 1);
+    auto fetch = [&](int64_t i) -> zr_status {  // gradient chunk i -> slot i % kSlots
+        const int k = (int)(i % kSlots);
         if (hipMemcpyAsync(gslot[k], g + i * chunk, 2 * len_of(i), hipMemcpyDeviceToHost, str) != hipSuccess ||
-            hipEventRecord(ev.e[k], str) != hipSuccess)
+            hipEventRecord(fetched[k], str) != hipSuccess)
             return fail(ZR_EHIP, "%s: gradient copy of chunk %lld failed", who, (long long)i);
         return ZR_OK;
     };
@@ -438,32 +475,29 @@ extern "C" zr_status zr_offload_adamw_step(const void *grad, float *master, floa
     // so that the caller may free or reuse the staging buffer at once.
     auto bail = [&](zr_status e) {
         (void)hipStreamSynchronize(str);
+        if (up)
+            (void)hipStreamSynchronize(up);
         return e;
     };
 
-    st = fetch(0);
-    if (st == ZR_OK && nchunks > 1)
-        st = fetch(1);
-    if (st != ZR_OK)
-        return bail(st);
-    for (int64_t i = 0; i < nchunks; ++i) {
-        const int k = (int)(i & 1);
-        const int64_t off = i * chunk, len = len_of(i);
-        if ((st = wait_event(ev.e[k], who)) != ZR_OK)
+    for (int64_t i = 0; i < kSlots && i < nchunks; ++i)
+        if ((st = fetch(i)) != ZR_OK)
             return bail(st);
-        if (pd && i >= 2 && (st = wait_event(ev.e[2 + k], who)) != ZR_OK)  // parameter slot k is free again
+    for (int64_t i = 0; i < nchunks; ++i) {
+        const int k = (int)(i % kSlots);
+        const int64_t off = i * chunk, len = len_of(i);
+        if ((st = wait_event(fetched[k], who)) != ZR_OK)
+            return bail(st);
+        if (pd && i >= kSlots && (st = wait_event(sent[k], who)) != ZR_OK)  // parameter slot k is free again
             return bail(st);
         host_step(gslot[k], master + off, exp_avg + off, exp_avg_sq + off, pd ? pslot[k] : nullptr, len, s, threads);
-        if (pd && (hipMemcpyAsync(pd + off, pslot[k], 2 * len, hipMemcpyHostToDevice, str) != hipSuccess ||
-                   hipEventRecord(ev.e[2 + k], str) != hipSuccess))
+        if (pd && (hipMemcpyAsync(pd + off, pslot[k], 2 * len, hipMemcpyHostToDevice, up) != hipSuccess ||
+                   hipEventRecord(sent[k], up) != hipSuccess))
             return bail(fail(ZR_EHIP, "%s: parameter copy of chunk %lld failed", who, (long long)i));
-        if (i + 2 < nchunks && (st = fetch(i + 2)) != ZR_OK)
+        if (i + kSlots < nchunks && (st = fetch(i + kSlots)) != ZR_OK)
             return bail(st);
     }
-    if (pd) {
-        for (int k = 0; k < 2 && k < nchunks; ++k)
-            if ((st = wait_event(ev.e[2 + k], who)) != ZR_OK)
-                return bail(st);
-    }
+    if (pd && (st = wait_event(sent[(nchunks - 1) % kSlots], who)) != ZR_OK)  // the last parameter copy
+        return bail(st);
     return ZR_OK;
 }
