@@ -38,7 +38,6 @@
 namespace zr {
 
 constexpr int64_t kTileChunks = kBlock;  // 16-byte chunks per tile: one per lane
-constexpr int kXcds = 8;                 // MI355X: workgroups go round-robin to 8 XCDs
 constexpr int kMaxDesc = 96;             // 3 KB of descriptors per launch
 
 struct CopyDesc {
@@ -88,8 +87,7 @@ __device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 b, uint32_t shift_bytes)
 __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch, int64_t total_tiles)
 {
     // grid is a multiple of kXcds; spare workgroups past the last tile exit
-    const int64_t per_xcd = gridDim.x / kXcds;
-    const int64_t tile = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const int64_t tile = xcd_first_tile();
     if (tile >= total_tiles)
         return;
     int lo = 0, hi = batch.count - 1;

@@ -93,13 +93,16 @@ __device__ __forceinline__ uint32_t reduce_one_f16(const ContribTable<MaxN> &c, 
     return f32_to_f16(finish_mean(sum, d));
 }
 
-template <int MaxN>
+// Tiles of kBlock groups, in XCD runs when kXcd (grid a multiple of 8), as the
+// bf16 reduce.
+template <int MaxN, bool kXcd>
 __global__ __launch_bounds__(kBlock) void reduce_f16_vec_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
                                                                 int64_t numel, int64_t head, int64_t groups,
                                                                 MeanDivisor d, zr_loss_scale *ls)
 {
     u32x4 *o4 = reinterpret_cast<u32x4 *>(out + head);
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    const int64_t first = kXcd ? xcd_first_tile() : (int64_t)blockIdx.x;
+    for (int64_t i = first * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         float acc[8];
         for (int32_t k = 0; k < n; k += 4) {
             u32x4 x[4];
@@ -277,10 +280,15 @@ static zr_status reduce_f16_launch(const void *const *contribs, int32_t n, int64
     if (!vec)
         return launch(reduce_f16_scalar_kernel<MaxN>, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st,
                       c, n, out, numel, d, ls);
-    const int64_t groups = (numel - head) / 8;
-    size_t lds = n > 8 ? 80 * 1024 : (n > 4 ? 40 * 1024 : 0);
-    return launch(reduce_f16_vec_kernel<MaxN>, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock), lds, st, c, n,
-                  out, numel, head, groups, d, ls);
+    // residency cap and tile order as the bf16 reduce
+    const int64_t groups = (numel - head) / 8, tiles = (groups + kBlock - 1) / kBlock;
+    const size_t lds = n > 8 ? 80 * 1024 : (n > 4 ? 40 * 1024 : 32 * 1024);
+    if constexpr (MaxN <= 8)
+        return launch(reduce_f16_vec_kernel<MaxN, true>, xcd_grid_of(tiles), dim3(kBlock), lds, st, c, n, out, numel,
+                      head, groups, d, ls);
+    else
+        return launch(reduce_f16_vec_kernel<MaxN, false>, grid_of(tiles), dim3(kBlock), lds, st, c, n, out, numel,
+                      head, groups, d, ls);
 }
 
 inline zr_status check_ls(const char *who, const void *ls)

@@ -9,10 +9,13 @@
 // contribution loads are issued four at a time so several 16-byte reads are in
 // flight per lane.  With n + 1 concurrent streams the DRAM rows thrash when
 // every CU is full of waves, so the kernel caps its residency with LDS it
-// reserves and never touches: 4 workgroups per CU for 5..8 contributions, 2 for
-// more (measured on MI355X: n = 8 5.6 -> 6.0 TB/s, n = 64 5.8 -> 6.3 TB/s;
-// n <= 4 is best uncapped).  The n device pointers travel by value in the
-// kernel arguments.
+// reserves and never touches, and for up to 8 contributions it deals its tiles
+// to the XCDs in contiguous runs.  Measured on MI355X against uncapped, default
+// order, on the same buffers: n = 4 at 5 workgroups per CU with the XCD order
+// 6.06 -> 6.43 TB/s; n = 8 at 4 per CU with the XCD order 5.66 -> 5.99 TB/s
+// (the cap alone gained nothing at n <= 8 in this arrangement); n = 64 at 2 per
+// CU in the default order 5.8 -> 6.1-6.3 TB/s, where the XCD order lost a
+// tenth.  The n device pointers travel by value in the kernel arguments.
 //
 // Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
 // blog (111qqz.com), "ZeRO-2: why gradients can be sharded too" (ReduceScatter
@@ -32,8 +35,9 @@ inline size_t residency_cap_lds(int32_t n)
         return 80 * 1024;  // 2 workgroups per CU
     if (n > 4)
         return 40 * 1024;  // 4 workgroups per CU
-    return 0;
+    return 32 * 1024;      // 5 workgroups per CU
 }
+
 
 __device__ __forceinline__ void add8(float (&acc)[8], u32x4 x)
 {
@@ -60,16 +64,18 @@ __device__ __forceinline__ void set8(float (&acc)[8], u32x4 x)
 }
 
 // Vector body over `groups` groups of 8 elements from element `head` (where
-// every contribution and the output are 16-byte aligned); block 0 also does
-// the unaligned head [0, head) and the tail element-wise.  out may be
-// c.p[0]: each lane reads all its inputs before it writes.
-template <int MaxN>
+// every contribution and the output are 16-byte aligned), in tiles of kBlock
+// groups (in XCD runs when kXcd, from a grid that is a multiple of 8); block 0
+// also does the unaligned head [0, head) and the tail element-wise.  out may
+// be c.p[0]: each lane reads all its inputs before it writes.
+template <int MaxN, bool kXcd>
 __global__ __launch_bounds__(kBlock) void reduce_vec_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
                                                             int64_t numel, int64_t head, int64_t groups,
                                                             MeanDivisor d)
 {
     u32x4 *o4 = reinterpret_cast<u32x4 *>(out + head);
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    const int64_t first = kXcd ? xcd_first_tile() : (int64_t)blockIdx.x;
+    for (int64_t i = first * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         float acc[8];
         for (int32_t k = 0; k < n; k += kLoadBatch) {
             u32x4 x[kLoadBatch];
@@ -125,9 +131,13 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
     for (int32_t k = 0; k < n && vec; ++k)
         vec = aligned_to(c.p[k] + head, 16);
     if (vec) {
-        int64_t groups = (numel - head) / 8;
-        return launch(reduce_vec_kernel<MaxN>, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock),
-                      residency_cap_lds(n), st, c, n, out, numel, head, groups, d);
+        const int64_t groups = (numel - head) / 8, tiles = (groups + kBlock - 1) / kBlock;
+        if constexpr (MaxN <= 8)  // tiles in XCD runs for up to 8 contributions
+            return launch(reduce_vec_kernel<MaxN, true>, xcd_grid_of(tiles), dim3(kBlock), residency_cap_lds(n), st,
+                          c, n, out, numel, head, groups, d);
+        else
+            return launch(reduce_vec_kernel<MaxN, false>, grid_of(tiles), dim3(kBlock), residency_cap_lds(n), st, c,
+                          n, out, numel, head, groups, d);
     }
     return launch(reduce_scalar_kernel<MaxN>, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, c, n,
                   out, numel, d);

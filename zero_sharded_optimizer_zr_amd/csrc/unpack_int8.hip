@@ -41,7 +41,6 @@ namespace {
 
 constexpr int kPerLane = 2;                          // 8-element chunks per lane
 constexpr int64_t kTileLanes = kBlock * kPerLane;  // 8-element chunks per tile
-constexpr int kXcds = 8;
 constexpr int kMaxDesc = 64;            // 64 * 48 B of descriptors per launch
 
 struct QDesc {
@@ -128,8 +127,7 @@ __device__ __forceinline__ void rebuild_chunks(const u32x2 *s2, uint32_t shift, 
 __global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64_t total_tiles)
 {
     // grid is a multiple of kXcds; spare workgroups past the last tile exit
-    const int64_t per_xcd = gridDim.x / kXcds;
-    const int64_t tile = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+    const int64_t tile = xcd_first_tile();
     if (tile >= total_tiles)
         return;
     int lo = 0, hi = batch.count - 1;

@@ -91,4 +91,15 @@ __device__ __forceinline__ float sqrt_rn(float x)
 __device__ __forceinline__ int64_t global_tid() { return (int64_t)blockIdx.x * kBlock + threadIdx.x; }
 __device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * kBlock; }
 
+// MI355X deals workgroups round-robin to its 8 XCDs (workgroup b runs on XCD
+// b mod 8), each with its own L2.  With a grid that is a multiple of kXcds,
+// tile (b mod 8) * (grid / 8) + b / 8 gives every XCD one contiguous run of
+// tiles instead of every eighth one; the next tile of a workgroup that loops
+// is gridDim.x further on.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_first_tile()
+{
+    return (int64_t)(blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
+}
+
 }  // namespace zr

@@ -43,6 +43,18 @@ inline dim3 grid_of(int64_t blocks)
     return dim3((unsigned)blocks);
 }
 
+// Grid for `tiles` tiles dealt to the XCDs in contiguous runs: a multiple of
+// 8, clamped to what one launch dimension allows (kernels loop over the rest).
+inline dim3 xcd_grid_of(int64_t tiles)
+{
+    if (tiles < 1)
+        tiles = 1;
+    tiles = (tiles + 7) / 8 * 8;
+    if (tiles > 0x7ffffff8)
+        tiles = 0x7ffffff8;
+    return dim3((unsigned)tiles);
+}
+
 inline bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 inline bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
