@@ -61,15 +61,15 @@ def kernel_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(per_launch_bytes):
+def measured_traffic(workload):
     """HBM bytes per AdamW launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    counts (scaled by the copy-kernel calibration), if they were taken on the
-    current kernel source; else None."""
+    counts (scaled by the copy-kernel calibration), if they were taken on this
+    workload and the current kernel source; else None."""
     if not os.path.exists(COUNTERS):
         return None
     with open(COUNTERS) as f:
         c = json.load(f)
-    if c.get("kernel_hash") != kernel_hash():
+    if c.get("kernel_hash") != kernel_hash() or c.get("workload") != workload:
         return None
     return c.get("traffic_bytes_per_launch")
 
@@ -237,7 +237,7 @@ def main():
     step_bytes = sum(bytes_per.values())
     adamw_ms = kernels["adamw"]["ms_avg"]
     achieved = bytes_per["adamw"] / (adamw_ms * 1e-3) / 1e9
-    traffic = measured_traffic(bytes_per["adamw"])
+    traffic = measured_traffic(w.name)
 
     fbytes = {"pack": 4 * S, "reduce_adamw": (2 * n + 26) * S, "unpack": 4 * S}
     fkernels = {}
