@@ -13,8 +13,9 @@ already resident in HBM when the timed region starts.
 Prints ONE JSON line.  `value` is shard elements per second of the whole step;
 `roofline` is the fused AdamW kernel's algorithmic HBM bandwidth (28 bytes per
 element) from HIP events around each of its launches, against the 8 TB/s
-MI355X peak; `cpu_baseline` is the oracle, as it stands, timed on the host
-cores over a bounded prefix of the same shard.
+MI355X peak (and, as a second figure, against the library's copy kernel moving
+the fp32 master in the same run); `cpu_baseline` is the oracle, as it stands,
+timed on the host cores over a bounded prefix of the same shard.
 """
 import argparse
 import hashlib
@@ -218,6 +219,25 @@ def main():
     torch.cuda.synchronize()
     felapsed = time.perf_counter() - fstart
 
+    # a plain device copy of the fp32 master by the library's copy kernel (one
+    # 2S-element bf16 "tensor", 4S bytes read + 4S written): the two-stream
+    # ceiling the AdamW rate is also quoted against
+    copy_lay = zr.zr_layout_create([2 * S], 1, 0)
+    copy_src = [(master.view(torch.int16), 0)]
+    copy_dst = torch.empty(2 * S, dtype=torch.int16, device=dev)
+    copy_ms = []
+    for r in range(args.warmup + args.steps):
+        x, y = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        x.record(stream)
+        zr.zr_pack(copy_lay, copy_src, copy_dst, 0, 2 * S, stream=stream)
+        y.record(stream)
+        if r >= args.warmup:
+            copy_ms.append((x, y))
+    torch.cuda.synchronize()
+    copy_avg = float(np.mean([x.elapsed_time(y) for x, y in copy_ms]))
+    copy_gbps = 8 * S / (copy_avg * 1e-3) / 1e9
+    del copy_dst, copy_src, copy_lay
+
     for _ in range(args.copy_calibration):
         a = torch.empty(1 << 31, dtype=torch.int16, device=dev)
         c = torch.empty_like(a)
@@ -230,8 +250,8 @@ def main():
     for k in names:
         ms = [x.elapsed_time(y) for x, y in events[k]]
         avg = float(np.mean(ms))
-        kernels[k] = {"ms_avg": round(avg, 4), "ms_min": round(float(np.min(ms)), 4),
-                      "algorithmic_bytes": bytes_per[k],
+        kernels[k] = {"ms_avg": round(avg, 4), "ms_median": round(float(np.median(ms)), 4),
+                      "ms_min": round(float(np.min(ms)), 4), "algorithmic_bytes": bytes_per[k],
                       "GBps": round(bytes_per[k] / (avg * 1e-3) / 1e9, 1)}
     ms_per_step = elapsed / args.steps * 1e3
     step_bytes = sum(bytes_per.values())
@@ -268,7 +288,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "zr_adamw_step", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": bytes_per["adamw"],
-                     "bytes_per_element": 28},
+                     "bytes_per_element": 28, "copy_ceiling": round(copy_gbps, 1),
+                     "frac_of_copy_ceiling": round(achieved / copy_gbps, 4)},
         "kernels": kernels,
         "fused_path": {"path": "pack+reduce_adamw+unpack", "ms_per_step": round(fms, 4),
                        "value": S / (fms * 1e-3), "unit": "elements/s",
