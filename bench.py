@@ -180,6 +180,16 @@ def main():
             for k, (x, y) in zip(names, ((t0, t1), (t1, t2), (t2, t3), (t3, t4))):
                 events[k].append((x, y))
 
+    # bring the GPU out of its idle clocks before the warm-up steps (a small
+    # shard's whole timed region is a few milliseconds): 0.25 s of a throwaway
+    # elementwise op on a scratch buffer
+    spin = torch.zeros(1 << 24, device=dev)
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < 0.25:
+        spin.add_(1.0)
+        torch.cuda.synchronize()
+    del spin
+
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
