@@ -4,6 +4,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -63,16 +64,45 @@ PIN_TESTS = ["tests/test_oracle_numerics.py", "tests/test_oracle_layout.py", "te
              "tests/test_oracle_fp16.py", "tests/test_oracle_int8.py"]
 
 
-@pytest.mark.parametrize("what,path,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_planted_mistake_is_caught(tmp_path, what, path, old, new):
+def _plant_and_run(root, what, path, old, new):
+    """Copies the oracle and its pins under `root`, plants one mistake and runs
+    the pins there; returns (returncode, stdout)."""
     for d in ("oracle", "tests", "zr_workloads"):
-        shutil.copytree(os.path.join(ROOT, d), tmp_path / d,
+        shutil.copytree(os.path.join(ROOT, d), os.path.join(root, d),
                         ignore=shutil.ignore_patterns("*.so", "__pycache__"))
-    target = tmp_path / path
-    text = target.read_text()
-    assert text.count(old) >= 1, f"mutation anchor not found: {old!r}"
-    target.write_text(text.replace(old, new))
+    target = os.path.join(root, path)
+    with open(target) as f:
+        text = f.read()
+    if text.count(old) < 1:
+        return None, f"mutation anchor not found: {old!r}"
+    with open(target, "w") as f:
+        f.write(text.replace(old, new))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_TESTS],
-                       cwd=tmp_path, capture_output=True, text=True, timeout=600)
-    assert r.returncode != 0, f"planted mistake '{what}' passed every pin:\n{r.stdout[-2000:]}"
-    assert "failed" in r.stdout
+                       cwd=root, capture_output=True, text=True, timeout=600)
+    return r.returncode, r.stdout
+
+
+_futures = {}
+
+
+def _result(tmp_path_factory, what):
+    """Outside pytest-xdist the first test starts every mutation at once on a
+    few host cores; each test then waits for its own."""
+    if os.environ.get("PYTEST_XDIST_WORKER"):
+        m = next(x for x in MUTATIONS if x[0] == what)
+        return _plant_and_run(str(tmp_path_factory.mktemp("mut")), *m)
+    if not _futures:
+        workers = max(2, len(os.sched_getaffinity(0)) // 2)
+        pool = ThreadPoolExecutor(max_workers=workers)
+        for m in MUTATIONS:
+            _futures[m[0]] = pool.submit(_plant_and_run, str(tmp_path_factory.mktemp("mut")), *m)
+        pool.shutdown(wait=False)
+    return _futures[what].result()
+
+
+@pytest.mark.parametrize("what", [m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(tmp_path_factory, what):
+    code, out = _result(tmp_path_factory, what)
+    assert code is not None, out
+    assert code != 0, f"planted mistake '{what}' passed every pin:\n{out[-2000:]}"
+    assert "failed" in out
