@@ -500,12 +500,14 @@ def cpu_baseline(w, lay, frags, b, sample, own_grad, contribs, st, hp, t_step, m
     param = np.empty(sample, np.uint16)
     cuts = np.linspace(0, sample, cores + 1).astype(np.int64)
 
-    def part(i):
-        lo, hi = int(cuts[i]), int(cuts[i + 1])
+    def span(lo, hi):
         contrib0[lo:hi] = oracle.pack(ref, views, b + lo, b + hi)
         oracle.reduce([contrib0[lo:hi]] + [p[lo:hi] for p in peers], out=grad[lo:hi])
         oracle.adamw(grad[lo:hi], master[lo:hi], m[lo:hi], v[lo:hi], param[lo:hi], step=t_step, **hp)
         oracle.unpack(ref, param[lo:hi], b + lo, b + hi, out_views)
+
+    def part(i):
+        span(int(cuts[i]), int(cuts[i + 1]))
 
     reps = 0
     with ThreadPoolExecutor(cores) as pool:
@@ -516,6 +518,16 @@ def cpu_baseline(w, lay, frags, b, sample, own_grad, contribs, st, hp, t_step, m
             secs = time.perf_counter() - t0
             if secs >= min_seconds:
                 break
+    # one thread over a shorter prefix, for the per-core rate
+    one = min(sample, 1 << 24)
+    reps1 = 0
+    t1 = time.perf_counter()
+    while True:
+        span(0, one)
+        reps1 += 1
+        secs1 = time.perf_counter() - t1
+        if secs1 >= min(2.0, min_seconds):
+            break
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -524,7 +536,9 @@ def cpu_baseline(w, lay, frags, b, sample, own_grad, contribs, st, hp, t_step, m
         pass
     return {"value": sample * reps / secs, "unit": "elements/s", "cores": cores, "kind": "oracle",
             "sample": f"first {sample} elements of the same shard, whole step (pack, reduce, AdamW, unpack) "
-                      f"repeated {reps} times: {secs:.2f} s on {cores} threads of {cpu}"}
+                      f"repeated {reps} times: {secs:.2f} s on {cores} threads of {cpu}",
+            "single_thread": {"value": one * reps1 / secs1, "unit": "elements/s",
+                              "sample": f"first {one} elements, {reps1} steps on one thread: {secs1:.2f} s"}}
 
 
 if __name__ == "__main__":
