@@ -39,6 +39,10 @@
  *     buffers 4-byte alignment (else ZR_EALIGN); 16-byte alignment is not
  *     required and gives the same bits as aligned buffers.
  *   - bf16 data is passed as raw 16-bit patterns (void*).
+ *   - Two environment variables exist for testing and change no result:
+ *     ZR_MAX_GRID (an integer >= 8) caps the workgroups of every launch -- each
+ *     kernel loops over the work its grid does not cover; ZR_HOST_SIMD
+ *     ("avx2" or "scalar") caps the instruction set of the host AdamW.
  */
 #ifndef ZR_H
 #define ZR_H
@@ -351,10 +355,9 @@ ZR_API zr_status zr_loss_scale_update(zr_loss_scale *ls, int32_t window, float f
  *
  * block is 256, 512, 1024 or 2048.  scales has ceil(numel / block) fp32
  * entries.  bf16 buffers need 2-byte and scales 4-byte alignment (else
- * ZR_EALIGN); q has no alignment rule, and buffers that are 8-byte (bf16) and
- * 4-byte (int8) aligned take the vector path (same bits).  No two buffers may
- * overlap.  numel == 0 is a no-op.  Errors: ZR_EINVAL, ZR_EALIGN, ZR_ERANGE,
- * ZR_EHIP.
+ * ZR_EALIGN); q has no alignment rule, and buffers that are 16-byte (bf16)
+ * and 8-byte (int8) aligned take the vector path (same bits).  No two buffers
+ * may overlap.  numel == 0 is a no-op.  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
  */
 ZR_API zr_status zr_quantize_int8(const void *src, int64_t numel, int32_t block, int8_t *q, float *scales,
                                   void *stream);

@@ -84,12 +84,8 @@ __device__ __forceinline__ u32x4 funnel(u32x4 a, u32x4 b, uint32_t shift_bytes)
     }
 }
 
-__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch, int64_t total_tiles)
+__device__ __forceinline__ void copy_tile(const CopyBatch &batch, int64_t tile)
 {
-    // grid is a multiple of kXcds; spare workgroups past the last tile exit
-    const int64_t tile = xcd_first_tile();
-    if (tile >= total_tiles)
-        return;
     int lo = 0, hi = batch.count - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -130,6 +126,14 @@ __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch, int64_t t
     }
 }
 
+// Tiles in XCD runs (the grid is a multiple of kXcds); a workgroup takes tile
+// xcd_first_tile(), then every gridDim.x-th after it.
+__global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch, int64_t total_tiles)
+{
+    for (int64_t tile = xcd_first_tile(); tile < total_tiles; tile += gridDim.x)
+        copy_tile(batch, tile);
+}
+
 namespace {
 
 struct Piece {
@@ -161,10 +165,7 @@ zr_status launch_pieces(const std::vector<Piece> &pieces, hipStream_t st)
             ++i;
         }
         batch.count = count;
-        int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
-        if (blocks > (int64_t)INT32_MAX)
-            return fail(ZR_ERANGE, "pack/unpack: fragment too large for one launch");
-        zr_status s = launch(copy_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, batch, tiles);
+        zr_status s = launch(copy_kernel, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
         if (s != ZR_OK)
             return s;
     }

@@ -223,37 +223,38 @@ template <int B>
 __global__ __launch_bounds__(kBlock) void quantize_vec_kernel(const uint16_t *src, int64_t numel, int8_t *q,
                                                               float *scales, int64_t ntiles)
 {
-    // workgroups in XCD runs (grid a multiple of 8), kBlock / 64 tiles each
-    const int64_t tile = xcd_first_tile() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (tile >= ntiles)
-        return;
+    // workgroups in XCD runs (grid a multiple of 8), kBlock / 64 tiles each,
+    // then the same again gridDim.x workgroups further on
     const int lane = threadIdx.x & 63;
-    const int64_t base = tile * kTile;
-    if (base + kTile <= numel)
-        quantize_tile<B, true>(src, numel, q, scales, base, lane);
-    else
-        quantize_tile<B, false>(src, numel, q, scales, base, lane);
+    const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
+    for (int64_t tile = xcd_first_tile() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         tile < ntiles; tile += stride) {
+        const int64_t base = tile * kTile;
+        if (base + kTile <= numel)
+            quantize_tile<B, true>(src, numel, q, scales, base, lane);
+        else
+            quantize_tile<B, false>(src, numel, q, scales, base, lane);
+    }
 }
 
 // Element-wise path for any natural alignment: one wave per block.
 __global__ __launch_bounds__(kBlock) void quantize_scalar_kernel(const uint16_t *src, int64_t numel, int32_t B,
                                                                  int8_t *q, float *scales, int64_t nblocks)
 {
-    const int64_t blk = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-    if (blk >= nblocks)
-        return;
     const int lane = threadIdx.x & 63;
-    const int64_t lo = blk * B;
-    const int64_t hi = lo + B < numel ? lo + B : numel;
-    float amax = 0.0f;
-    for (int64_t i = lo + lane; i < hi; i += 64)
-        amax = fmaxf(amax, fabsf(bf16_to_f32(src[i])));
-    amax = wave_max(amax);
-    const float s = __fdiv_rn(amax, 127.0f);
-    if (lane == 0)
-        scales[blk] = s;
-    for (int64_t i = lo + lane; i < hi; i += 64)
-        q[i] = (int8_t)quantize_one(bf16_to_f32(src[i]), s);
+    for (int64_t blk = wave_id(); blk < nblocks; blk += (int64_t)gridDim.x * (kBlock / 64)) {
+        const int64_t lo = blk * B;
+        const int64_t hi = lo + B < numel ? lo + B : numel;
+        float amax = 0.0f;
+        for (int64_t i = lo + lane; i < hi; i += 64)
+            amax = fmaxf(amax, fabsf(bf16_to_f32(src[i])));
+        amax = wave_max(amax);
+        const float s = __fdiv_rn(amax, 127.0f);
+        if (lane == 0)
+            scales[blk] = s;
+        for (int64_t i = lo + lane; i < hi; i += 64)
+            q[i] = (int8_t)quantize_one(bf16_to_f32(src[i]), s);
+    }
 }
 
 template <int B, bool kFull>
@@ -290,15 +291,14 @@ template <int B>
 __global__ __launch_bounds__(kBlock) void dequantize_vec_kernel(const int8_t *q, const float *scales, int64_t numel,
                                                                 uint16_t *dst, int64_t ntiles)
 {
-    const int64_t tile = wave_id();
-    if (tile >= ntiles)
-        return;
     const int lane = threadIdx.x & 63;
-    const int64_t base = tile * kTile;
-    if (base + kTile <= numel)
-        dequantize_tile<B, true>(q, scales, numel, dst, base, lane);
-    else
-        dequantize_tile<B, false>(q, scales, numel, dst, base, lane);
+    for (int64_t tile = wave_id(); tile < ntiles; tile += (int64_t)gridDim.x * (kBlock / 64)) {
+        const int64_t base = tile * kTile;
+        if (base + kTile <= numel)
+            dequantize_tile<B, true>(q, scales, numel, dst, base, lane);
+        else
+            dequantize_tile<B, false>(q, scales, numel, dst, base, lane);
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void dequantize_scalar_kernel(const int8_t *q, const float *scales,
@@ -339,14 +339,10 @@ extern "C" zr_status zr_quantize_int8(const void *src, int64_t numel, int32_t bl
     auto s = static_cast<const uint16_t *>(src);
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (!(aligned_to(s, 16) && aligned_to(q, 8))) {
-        if (nblocks > (int64_t)0x7fffffff * 4)
-            return fail(ZR_ERANGE, "zr_quantize_int8: too many blocks for one launch");
         return launch(quantize_scalar_kernel, grid_of((nblocks + 3) / 4), dim3(kBlock), 0, st, s, numel, block, q,
                       scales, nblocks);
     }
     const int64_t ntiles = (numel + kTile - 1) / kTile;
-    if ((ntiles + 3) / 4 > 0x7ffffff8)  // one tile per wave, no loop: the XCD grid must cover them
-        return fail(ZR_ERANGE, "zr_quantize_int8: numel too large for one launch");
     const dim3 grid = xcd_grid_of((ntiles + 3) / 4);
     constexpr size_t lds = 32 * 1024;  // 5 workgroups per CU
     switch (block) {
@@ -385,8 +381,6 @@ extern "C" zr_status zr_dequantize_int8(const int8_t *q, const float *scales, in
         return launch(dequantize_scalar_kernel, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, q,
                       scales, numel, block, d);
     const int64_t ntiles = (numel + kTile - 1) / kTile;
-    if ((ntiles + 3) / 4 > 0x7fffffff)
-        return fail(ZR_ERANGE, "zr_dequantize_int8: numel too large for one launch");
     const dim3 grid = grid_of((ntiles + 3) / 4);
     switch (block) {
     case 256: return launch(dequantize_vec_kernel<256>, grid, dim3(kBlock), 0, st, q, scales, numel, d, ntiles);

@@ -124,12 +124,8 @@ __device__ __forceinline__ void rebuild_chunks(const u32x2 *s2, uint32_t shift, 
     }
 }
 
-__global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64_t total_tiles)
+__device__ __forceinline__ void unpack_int8_tile(const QBatch &batch, int64_t tile)
 {
-    // grid is a multiple of kXcds; spare workgroups past the last tile exit
-    const int64_t tile = xcd_first_tile();
-    if (tile >= total_tiles)
-        return;
     int lo = 0, hi = batch.count - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -179,6 +175,14 @@ __global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64
     }
 }
 
+// Tiles in XCD runs (the grid is a multiple of kXcds); a workgroup takes tile
+// xcd_first_tile(), then every gridDim.x-th after it.
+__global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64_t total_tiles)
+{
+    for (int64_t tile = xcd_first_tile(); tile < total_tiles; tile += gridDim.x)
+        unpack_int8_tile(batch, tile);
+}
+
 zr_status launch_batches(const std::vector<QDesc> &pieces, int lg_block, hipStream_t st)
 {
     size_t i = 0;
@@ -200,10 +204,7 @@ zr_status launch_batches(const std::vector<QDesc> &pieces, int lg_block, hipStre
             ++i;
         }
         batch.count = count;
-        const int64_t blocks = (tiles + kXcds - 1) / kXcds * kXcds;
-        if (blocks > (int64_t)INT32_MAX)
-            return fail(ZR_ERANGE, "zr_unpack_int8: fragment too large for one launch");
-        zr_status s = launch(unpack_int8_kernel, dim3((unsigned)blocks), dim3(kBlock), 0, st, batch, tiles);
+        zr_status s = launch(unpack_int8_kernel, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
         if (s != ZR_OK)
             return s;
     }

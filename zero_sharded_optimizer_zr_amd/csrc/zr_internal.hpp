@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdlib>
 #include <functional>
 #include <tuple>
 #include <utility>
@@ -32,26 +33,38 @@ void clear_error();
 void for_each_fragment(const zr_layout &L, int64_t begin, int64_t end,
                        const std::function<void(const zr_fragment &)> &fn);
 
-// Grid of `blocks` workgroups, clamped to what one launch dimension allows
-// (kernels loop over any remainder).
+// Most workgroups one launch gets: what one grid dimension allows, or fewer
+// when the environment sets ZR_MAX_GRID (>= 8; a testing knob).  Every kernel
+// loops over the work its grid does not cover, so results never depend on it.
+inline int64_t max_grid()
+{
+    const char *s = std::getenv("ZR_MAX_GRID");
+    const long long v = s ? std::atoll(s) : 0;
+    return v >= 8 && v < 0x7fffffff ? (int64_t)v : (int64_t)0x7fffffff;
+}
+
+// Grid of `blocks` workgroups, clamped to max_grid() (kernels loop over any
+// remainder).
 inline dim3 grid_of(int64_t blocks)
 {
     if (blocks < 1)
         blocks = 1;
-    if (blocks > 0x7fffffff)
-        blocks = 0x7fffffff;
+    const int64_t cap = max_grid();
+    if (blocks > cap)
+        blocks = cap;
     return dim3((unsigned)blocks);
 }
 
 // Grid for `tiles` tiles dealt to the XCDs in contiguous runs: a multiple of
-// 8, clamped to what one launch dimension allows (kernels loop over the rest).
+// 8, clamped to max_grid() rounded down to 8 (kernels loop over the rest).
 inline dim3 xcd_grid_of(int64_t tiles)
 {
     if (tiles < 1)
         tiles = 1;
     tiles = (tiles + 7) / 8 * 8;
-    if (tiles > 0x7ffffff8)
-        tiles = 0x7ffffff8;
+    const int64_t cap = max_grid() / 8 * 8;
+    if (tiles > cap)
+        tiles = cap;
     return dim3((unsigned)tiles);
 }
 
