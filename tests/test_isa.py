@@ -1,0 +1,93 @@
+"""The gfx950 code of the streaming kernels has the shape their design states
+(CPU only: hipcc cross-compiles the device code to assembly here).
+
+For each hot kernel: every HBM access is a global (not flat) non-temporal load
+or store of the stated width, there is no LDS instruction (the residency caps
+reserve LDS but never touch it) and no scratch memory, and the number of
+vector memory instructions in the body is the one the data layout implies."""
+import os
+import re
+import subprocess
+import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, os.path.join(ROOT, "zero_sharded_optimizer_zr_amd"))
+import build as zr_build  # noqa: E402
+
+CSRC = os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "csrc")
+
+# (source, mangled-name fragment, {instruction: count in the body}).  The
+# counts are static instructions of the kernel body; the head/tail element
+# paths use narrow accesses, which are not pinned.
+#   AdamW: dwordx4 in/out of master, m, v; dwordx2 of gradient in, copy out.
+#   reduce (8-pointer table, XCD order): two batches of 4 contribution loads.
+#   fused: master/m/v as AdamW, 8 dwordx2 contribution loads, dwordx2 copy.
+#   copy: aligned or funnel-shifted (two) loads, one store per lane.
+#   int8 quantizer: 4 chunks of 16-byte loads per tile, 8-byte code stores.
+KERNELS = [
+    ("adamw.hip", "adamw_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
+                                            "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
+    ("reduce.hip", "reduce_vec_kernelILi8ELb1E", {"global_load_dwordx4": 8, "global_store_dwordx4": 1}),
+    ("fused.hip", "fused_vec_kernelILi8ELb1ELb0E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
+                                                    "global_load_dwordx2": 8, "global_store_dwordx2": 1}),
+    ("fp16.hip", "adamw_f16_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
+                                               "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
+    ("copy.hip", "copy_kernel", {"global_load_dwordx4": 2, "global_store_dwordx4": 1}),
+    ("unpack_int8.hip", "unpack_int8_kernel", {"global_store_dwordx4": 5}),
+    ("quant.hip", "quantize_vec_kernelILi2048E", {"global_load_dwordx4": 4, "global_store_dwordx2": 4}),
+]
+
+
+@pytest.fixture(scope="module")
+def asm():
+    """Device assembly of each source, compiled with the library's flags."""
+    tmp = tempfile.mkdtemp(prefix="zr_isa_")
+    files = sorted({k[0] for k in KERNELS})
+
+    def compile_one(name):
+        out = os.path.join(tmp, name + ".s")
+        cmd = ["hipcc", *zr_build.FLAGS, f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+               "--offload-device-only", "-S", os.path.join(CSRC, name), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        assert r.returncode == 0, r.stderr[-2000:]
+        with open(out) as f:
+            return name, f.read()
+
+    with ThreadPoolExecutor(len(files)) as pool:
+        return dict(pool.map(compile_one, files))
+
+
+def kernel_body(text, fragment):
+    """Instructions between the kernel's entry label and the end of its
+    function, and its metadata block."""
+    m = re.search(r"^(_Z\S*" + re.escape(fragment) + r"\S*):", text, re.M)
+    assert m, f"kernel {fragment} not found"
+    name = m.group(1)
+    start = m.end()
+    end = text.index(".Lfunc_end", start)
+    body = [ln.split(";")[0].strip() for ln in text[start:end].splitlines()]
+    meta = text[text.index(f".name:           {name}"):]
+    meta = meta[:meta.index("\n  - ") if "\n  - " in meta else len(meta)]
+    return [ln for ln in body if ln and not ln.startswith(".")], meta
+
+
+@pytest.mark.parametrize("src,frag,counts", KERNELS, ids=[k[1] for k in KERNELS])
+def test_kernel_shape(asm, src, frag, counts):
+    body, meta = kernel_body(asm[src], frag)
+    ops = [ln.split()[0] for ln in body]
+    assert not [o for o in ops if o.startswith("ds_")], "LDS instruction in a streaming kernel"
+    assert not [o for o in ops if o.startswith(("scratch_", "buffer_"))], "scratch or buffer access"
+    assert not [o for o in ops if o.startswith(("flat_load", "flat_store"))], "flat access (not global)"
+    assert not [o for o in ops if o.startswith(("s_store", "s_buffer_store", "s_atomic", "s_buffer_atomic",
+                                               "s_dcache_wb", "s_dcache_discard"))], "scalar-cache write"
+    assert re.search(r"\.private_segment_fixed_size:\s+0\b", meta), "kernel uses scratch memory"
+    for op, want in counts.items():
+        lines = [ln for ln in body if ln.split()[0] == op]
+        assert len(lines) == want, f"{op}: {len(lines)} in the body, expected {want}"
+        assert all(ln.rstrip().endswith(" nt") for ln in lines), f"{op} without the non-temporal hint"
+    wide = [ln for ln in body if ln.split()[0] in ("global_load_dwordx4", "global_store_dwordx4")]
+    assert wide, "no 16-byte global access"
