@@ -154,8 +154,6 @@ zr_status launch_pieces(const std::vector<Piece> &pieces, hipStream_t st)
             const Piece &p = pieces[i];
             int64_t body = (p.n - dst_head(p.dst, p.n)) / 8;
             int64_t nt = std::max<int64_t>(1, (body + kTileChunks - 1) / kTileChunks);
-            if (count > 0 && tiles + nt > (int64_t)INT32_MAX - kXcds)
-                break;
             batch.d[count].src = p.src;
             batch.d[count].dst = p.dst;
             batch.d[count].n = p.n;

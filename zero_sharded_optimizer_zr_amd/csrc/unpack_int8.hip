@@ -195,8 +195,6 @@ zr_status launch_batches(const std::vector<QDesc> &pieces, int lg_block, hipStre
             const QDesc &p = pieces[i];
             const int64_t body = (p.n - head_of(p.dst, p.n)) / 8;
             const int64_t nt = std::max<int64_t>(1, (body + kTileLanes - 1) / kTileLanes);
-            if (count > 0 && tiles + nt > (int64_t)INT32_MAX - kXcds)
-                break;
             batch.d[count] = p;
             batch.d[count].tile_begin = tiles;
             tiles += nt;
