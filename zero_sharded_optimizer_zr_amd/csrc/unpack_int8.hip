@@ -15,7 +15,8 @@
 // 8 per lane, 2048 elements apart, each one aligned 16-byte store; two chunks
 // in flight per lane measured 5.9-6.0 TB/s against 5.3 for one, and capping
 // residency only slowed it), found by a binary search over the batch's tile
-// prefix sums; tiles go to the 8 XCDs in contiguous runs.  Codes come in as
+// prefix sums; tiles go to the 8 XCDs in contiguous runs (a grid smaller than
+// the tile count loops, every gridDim.x-th tile).  Codes come in as
 // two aligned 8-byte words per lane, funnel-shifted (v_alignbyte) when the
 // source's byte phase differs from the destination's; a lane's 8 elements
 // span at most two blocks (blocks are >= 256 elements and a descriptor lies in
