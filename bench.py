@@ -298,7 +298,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "zr_adamw_step", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": bytes_per["adamw"],
-                     "bytes_per_element": 28, "copy_ceiling": round(copy_gbps, 1),
+                     "bytes_per_element": 28, "elements_per_s": S / (adamw_ms * 1e-3),
+                     "copy_ceiling": round(copy_gbps, 1),
                      "frac_of_copy_ceiling": round(achieved / copy_gbps, 4)},
         "kernels": kernels,
         "fused_path": {"path": "pack+reduce_adamw+unpack", "ms_per_step": round(fms, 4),
