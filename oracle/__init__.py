@@ -65,6 +65,10 @@ def _load():
         lib.zr_oracle_quantize_int8.restype = None
         lib.zr_oracle_dequantize_int8.argtypes = [p, p, i64, i32, p]
         lib.zr_oracle_dequantize_int8.restype = None
+        lib.zr_oracle_quantize_int4.argtypes = [p, i64, i32, p, p]
+        lib.zr_oracle_quantize_int4.restype = None
+        lib.zr_oracle_dequantize_int4.argtypes = [p, p, i64, i32, p]
+        lib.zr_oracle_dequantize_int4.restype = None
         _lib = lib
     return _lib
 
@@ -298,6 +302,32 @@ def dequantize_int8(q: np.ndarray, scales: np.ndarray, block: int) -> np.ndarray
     return out
 
 
+def quantize_int4(src: np.ndarray, block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric block-wise int4 quantization of bf16 bits (ZeRO++ qwZ names
+    int4 beside int8 on the concept page (compassingai.com); the int8 rule with
+    7 for 127): per block s = amax / 7, q = rint(x / s) clamped to +-7; two
+    codes per byte, element 2j in the low four bits of byte j.  Returns
+    (q4 uint8 [ceil(numel / 2)], scales fp32 [ceil(numel / block)])."""
+    _check(src, np.uint16, "src")
+    if block < 1:
+        raise ValueError("block must be >= 1")
+    q4 = np.empty(-(-src.size // 2), dtype=np.uint8)
+    scales = np.empty(-(-src.size // block), dtype=np.float32)
+    _load().zr_oracle_quantize_int4(_ptr(src), src.size, int(block), _ptr(q4), _ptr(scales))
+    return q4, scales
+
+
+def dequantize_int4(q4: np.ndarray, scales: np.ndarray, numel: int, block: int) -> np.ndarray:
+    """bf16 bits of q * s for the first numel codes of q4, rounded to nearest even."""
+    _check(q4, np.uint8, "q4")
+    _check(scales, np.float32, "scales")
+    if q4.size < -(-numel // 2) or scales.size != -(-numel // block):
+        raise ValueError("q4 or scales has the wrong length")
+    out = np.empty(numel, dtype=np.uint16)
+    _load().zr_oracle_dequantize_int4(_ptr(q4), _ptr(scales), numel, int(block), _ptr(out))
+    return out
+
+
 # ---------------------------------------------------------------- layout ----
 
 class Layout:
@@ -490,4 +520,52 @@ def unpack_int8(layout: Layout, q: np.ndarray, scales: np.ndarray, block: int, b
     i = np.arange(begin, end, dtype=np.int64)
     g = gathered_block(layout, i, block)
     x = q[: end - begin].astype(np.float32) * scales[g - g[0]]
+    unpack(layout, bf16_from_f32(x), begin, end, views)
+
+
+def quantize_gathered_int4(layout: Layout, flat: np.ndarray, block: int) -> Tuple[np.ndarray, np.ndarray]:
+    """The int4 quantized AllGather of the whole flat buffer: every rank r runs
+    quantize_int4 on its own shard flat[r S, (r+1) S) -- blocks and the packing
+    start afresh at every shard, ceil(S / 2) bytes and ceil(S / block) scales
+    per rank -- and the gather concatenates codes and scales in rank order."""
+    _check(flat, np.uint16, "flat")
+    if flat.size != layout.psi_pad:
+        raise ValueError("flat must hold psi_pad elements")
+    S = layout.shard
+    codes, scales = [], []
+    for r in range(layout.n_d):
+        q, s = quantize_int4(np.ascontiguousarray(flat[r * S:(r + 1) * S]), block)
+        codes.append(q)
+        scales.append(s)
+    return np.concatenate(codes), np.concatenate(scales)
+
+
+def gathered_code_byte(layout: Layout, i: np.ndarray) -> np.ndarray:
+    """Byte of the int4 gathered codes holding flat element i's code: rank
+    r = i // S, then byte (i - r S) // 2 of that rank's ceil(S / 2); the code is
+    in the high four bits when (i - r S) is odd."""
+    S = layout.shard
+    r = i // S
+    return r * (-(-S // 2)) + (i - r * S) // 2
+
+
+def unpack_int4(layout: Layout, q4: np.ndarray, scales: np.ndarray, block: int, begin: int, end: int,
+                views: Sequence[View]) -> None:
+    """Receiver side of the int4 quantized AllGather: flat elements [begin,
+    end) rebuilt as bf16(code * scale of their block) and scattered into the
+    views like unpack.  q4[0] is the byte holding element begin's code and
+    scales[0] the scale of the block holding element begin; the rest follow in
+    gathered order."""
+    _check(q4, np.uint8, "q4")
+    _check(scales, np.float32, "scales")
+    if end <= begin:
+        return
+    S = layout.shard
+    i = np.arange(begin, end, dtype=np.int64)
+    byte = gathered_code_byte(layout, i)
+    high = ((i - (i // S) * S) % 2).astype(np.uint8)
+    nibble = (q4[byte - byte[0]] >> (4 * high)) & 0xF
+    code = nibble.astype(np.int16) - 16 * (nibble >= 8)
+    g = gathered_block(layout, i, block)
+    x = code.astype(np.float32) * scales[g - g[0]]
     unpack(layout, bf16_from_f32(x), begin, end, views)

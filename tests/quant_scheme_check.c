@@ -1,13 +1,15 @@
 /*
  * Exhaustive check of the reciprocal-and-correction quotient that the int8
- * block quantizer uses in place of a division (CPU; test infrastructure).
+ * and int4 block quantizers use in place of a division (CPU; test
+ * infrastructure).  The argument is the largest code Q: 127 (int8, the
+ * default) or 7 (int4).
  *
- * For every positive finite bf16 absmax with s = RN(absmax / 127) >= 2^-100 and
+ * For every positive finite bf16 absmax with s = RN(absmax / Q) >= 2^-100 and
  * every bf16 x with 0 <= x <= absmax:
  *   r  = RN(1 / s)
  *   q0 = RN(x * r);  rem = RN(x - q0 * s) (fused);  q1 = RN(q0 + rem * r) (fused)
- * and the code clamp(rint(q1), -127, 127) is compared with the definition
- * clamp(rint(RN(x / s)), -127, 127).  Negative x need no separate pass: every
+ * and the code clamp(rint(q1), -Q, Q) is compared with the definition
+ * clamp(rint(RN(x / s)), -Q, Q).  Negative x need no separate pass: every
  * step is odd in x under round-to-nearest-even, so the code of -x is minus the
  * code of x.
  *
@@ -18,19 +20,23 @@
 #include <math.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 static float from_bits(uint32_t u) { float f; memcpy(&f, &u, sizeof f); return f; }
 static uint32_t to_bits(float f) { uint32_t u; memcpy(&u, &f, sizeof u); return u; }
-static float code(float t) { return fminf(fmaxf(rintf(t), -127.0f), 127.0f); }
+static float Q = 127.0f;
+static float code(float t) { return fminf(fmaxf(rintf(t), -Q), Q); }
 
-int main(void)
+int main(int argc, char **argv)
 {
+    if (argc > 1)
+        Q = (float)atoi(argv[1]);
     long long pairs = 0, bad_code = 0, bad_quot = 0, bad_plain = 0;
 #pragma omp parallel for schedule(dynamic, 64) reduction(+ : pairs, bad_code, bad_quot, bad_plain)
     for (int a = 1; a < 0x7f80; ++a) {
         const float amax = from_bits((uint32_t)a << 16);
-        const float s = amax / 127.0f;
+        const float s = amax / Q;
         if (to_bits(s) < 0x0d800000u)  /* s < 2^-100: the quantizer divides */
             continue;
         const float r = 1.0f / s;

@@ -56,12 +56,19 @@ MUTATIONS = [
      "return i // block"),
     ("sub-range scales not offset", PY, "x = q[: end - begin].astype(np.float32) * scales[g - g[0]]",
      "x = q[: end - begin].astype(np.float32) * scales[g - g[0] + (1 if begin > 0 else 0)]"),
+    ("int4 nibbles swapped", C, "q4[i / 2] |= (i % 2) ? (uint8_t)(nibble << 4) : nibble;",
+     "q4[i / 2] |= (i % 2) ? nibble : (uint8_t)(nibble << 4);"),
+    ("int4 scale over 8", C, "float s = amax / 7.0f;", "float s = amax / 8.0f;"),
+    ("int4 clamp at 6", C, "if (r > 7.0f)\n                    r = 7.0f;", "if (r > 6.0f)\n                    r = 6.0f;"),
+    ("int4 codes read unsigned", C, "int code = nibble >= 8 ? nibble - 16 : nibble;", "int code = nibble;"),
+    ("int4 gathered bytes not restarted per shard", PY, "return r * (-(-S // 2)) + (i - r * S) // 2",
+     "return i // 2"),
     ("unpack reversed", PY, "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n]",
      "arr[toff - first: toff - first + n] = flat[foff - begin: foff - begin + n][::-1]"),
 ]
 
 PIN_TESTS = ["tests/test_oracle_numerics.py", "tests/test_oracle_layout.py", "tests/test_oracle_ledger.py",
-             "tests/test_oracle_fp16.py", "tests/test_oracle_int8.py"]
+             "tests/test_oracle_fp16.py", "tests/test_oracle_int8.py", "tests/test_oracle_int4.py"]
 
 
 def _plant_and_run(root, what, path, old, new):
