@@ -403,8 +403,9 @@ def qwz_leg(w, lay, info, b, S, flat_param, args, stream):
     bf16 shard (zr_quantize_int8), and the gathered codes and scales of the
     flat range [0, G) -- G = psi_pad, or at most --qwz-max-gather elements, the
     rest of the ranks' codes synthetic -- are rebuilt straight into the bf16
-    tensor views (zr_unpack_int8).  The plain bf16 unpack of the same range
-    (zr_unpack from a bf16 flat buffer) is timed beside it."""
+    tensor views (zr_unpack_int8); the same with int4 codes, two per byte
+    (zr_quantize_int4, zr_unpack_int4).  The plain bf16 unpack of the same range
+    (zr_unpack from a bf16 flat buffer) is timed beside them."""
     import torch
 
     import zero_sharded_optimizer_zr_amd as zr
@@ -420,6 +421,9 @@ def qwz_leg(w, lay, info, b, S, flat_param, args, stream):
     scales = torch.rand(ranks * per_rank, dtype=torch.float32, device=dev, generator=gen) * 1e-3
     r = w.rank if w.rank < ranks else 0
     my_codes, my_scales = codes[r * S:(r + 1) * S], scales[r * per_rank:(r + 1) * per_rank]
+    nbytes = -(-S // 2)
+    codes4 = torch.randint(0, 256, (ranks * nbytes,), dtype=torch.uint8, device=dev, generator=gen)
+    my_codes4 = codes4[r * nbytes:(r + 1) * nbytes]
     views = [None] * len(w.numels)
     for t, toff, _, cnt in zr.zr_layout_fragments(lay, 0, G):
         views[t] = (torch.empty(cnt, dtype=torch.int16, device=dev), toff)
@@ -431,11 +435,16 @@ def qwz_leg(w, lay, info, b, S, flat_param, args, stream):
         ("unpack_int8", lambda: zr.zr_unpack_int8(lay, codes, scales, 0, G, views, block=block, stream=stream),
          3 * part + 4 * ranks * per_rank),
         ("unpack_bf16", lambda: zr.zr_unpack(lay, flat, 0, G, views, stream=stream), 4 * part),
+        ("quantize_int4", lambda: zr.zr_quantize_int4(flat_param, my_codes4, my_scales, block=block, stream=stream),
+         2 * S + nbytes + 4 * per_rank),
+        ("unpack_int4", lambda: zr.zr_unpack_int4(lay, codes4, scales, 0, G, views, block=block, stream=stream),
+         2 * part + -(-part // 2) + 4 * ranks * per_rank),
     ]
     _, stats = time_path(calls, args.warmup, args.steps, stream)
     out = {"block": block, "gathered_elements": G, "ranks_gathered": ranks,
-           "gather_payload_bytes": {"int8": G + 4 * ranks * per_rank, "bf16": 2 * G}, "kernels": stats}
-    del codes, scales, views, flat
+           "gather_payload_bytes": {"int8": G + 4 * ranks * per_rank, "int4": ranks * nbytes + 4 * ranks * per_rank,
+                                    "bf16": 2 * G}, "kernels": stats}
+    del codes, codes4, scales, views, flat
     torch.cuda.empty_cache()
     return out
 

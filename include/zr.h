@@ -388,6 +388,37 @@ ZR_API zr_status zr_dequantize_int8(const int8_t *q, const float *scales, int64_
 ZR_API zr_status zr_unpack_int8(const zr_layout *layout, const int8_t *q, const float *scales, int32_t block,
                                 int64_t begin, int64_t end, const zr_view *views, int32_t n_views, void *stream);
 
+/*
+ * int4 codes for the same AllGather.  [CON] ZeRO++ section names int4 beside
+ * int8 for qwZ and gives no details; the rule taken is the int8 one with 7 in
+ * place of 127: per block s = amax / 7, q = rint(x / s) clamped to [-7, 7]
+ * (q = 0 when s = 0), rebuilt as bf16(q * s).  Codes are 4-bit two's
+ * complement, two per byte: element 2j in the low four bits of byte j, element
+ * 2j + 1 in the high four bits; an odd count leaves 0 in the last byte's high
+ * four bits.
+ *
+ * zr_quantize_int4: q4 holds ceil(numel / 2) bytes, scales ceil(numel / block)
+ * fp32; buffer rules and errors as zr_quantize_int8 (q4 has no alignment rule;
+ * 16-byte bf16 and 4-byte code buffers take the vector path, same bits).
+ * zr_dequantize_int4: the inverse for numel elements.
+ */
+ZR_API zr_status zr_quantize_int4(const void *src, int64_t numel, int32_t block, uint8_t *q4, float *scales,
+                                  void *stream);
+ZR_API zr_status zr_dequantize_int4(const uint8_t *q4, const float *scales, int64_t numel, int32_t block, void *dst,
+                                    void *stream);
+
+/*
+ * Dequantize-on-unpack of an int4 AllGather: every rank quantizes its shard
+ * with zr_quantize_int4, so blocks and the packing restart at every shard --
+ * ceil(S / 2) bytes and ceil(S / block) scales per rank -- and the gather
+ * concatenates them in rank order.  q4[0] is the byte that holds the code of
+ * flat element begin (in its high four bits when begin - r S is odd, r the
+ * rank of begin); scales[0] is the scale of the block that holds element
+ * begin.  Otherwise as zr_unpack_int8.
+ */
+ZR_API zr_status zr_unpack_int4(const zr_layout *layout, const uint8_t *q4, const float *scales, int32_t block,
+                                int64_t begin, int64_t end, const zr_view *views, int32_t n_views, void *stream);
+
 /* ------------------------------------------------ ZeRO-Offload step ----- */
 
 /*

@@ -16,6 +16,7 @@ GUARD = 64
 GUARD_U16 = 0x5A5A
 GUARD_F32_BITS = 0x7FBADBAD  # a NaN pattern nobody computes
 GUARD_I8 = -128  # outside the int8 code range [-127, 127]
+GUARD_U8 = 0x88  # two int4 codes of -8, outside the int4 code range [-7, 7]
 
 
 def device():
@@ -55,6 +56,10 @@ class Placed:
             big = torch.full((offset + n + GUARD,), GUARD_I8, dtype=torch.int8)
             big[offset:offset + n] = torch.from_numpy(host.copy())
             self.guard_bits = np.int8(GUARD_I8)
+        elif host.dtype == np.uint8:
+            big = torch.full((offset + n + GUARD,), GUARD_U8, dtype=torch.uint8)
+            big[offset:offset + n] = torch.from_numpy(host.copy())
+            self.guard_bits = np.uint8(GUARD_U8)
         else:
             raise TypeError(host.dtype)
         self.big = big.to(dev)
@@ -64,13 +69,13 @@ class Placed:
     def host(self) -> np.ndarray:
         if self.view.dtype == torch.int16:
             return u16(self.view)
-        if self.view.dtype == torch.int8:
+        if self.view.dtype in (torch.int8, torch.uint8):
             return self.view.cpu().numpy().copy()
         return f32(self.view)
 
     def guards_intact(self) -> bool:
         b = self.big.cpu().numpy()
-        if b.dtype != np.int8:
+        if b.dtype not in (np.int8, np.uint8):
             b = b.view(np.uint16) if b.dtype == np.int16 else b.view(np.uint32)
         return bool(np.all(b[:self.offset] == self.guard_bits) and np.all(b[self.offset + self.n:] == self.guard_bits))
 

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 31
+    assert len(names) == 34
     lib = ctypes.CDLL(zr.LIBRARY)
     for name in names:
         assert hasattr(lib, name), name
@@ -355,6 +355,41 @@ def test_int8_validation():
 
 
 
+def test_int4_validation():
+    L = zr._lib
+    src, q, sc, dst = A, A + 2**22, A + 2**23, A + 2**24
+    for block in (0, 1, 128, 300, 4096, -256):
+        assert L.zr_quantize_int4(src, 1000, block, q, sc, None) == zr.ZR_EINVAL
+        assert L.zr_dequantize_int4(q, sc, 1000, block, dst, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int4(src, -1, 256, q, sc, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int4(None, 16, 256, q, sc, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int4(src, 16, 256, None, sc, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int4(src, 16, 256, q, None, None) == zr.ZR_EINVAL
+    assert L.zr_quantize_int4(src + 1, 16, 256, q, sc, None) == zr.ZR_EALIGN
+    assert L.zr_quantize_int4(src, 16, 256, q, sc + 2, None) == zr.ZR_EALIGN
+    assert L.zr_quantize_int4(src, 1000, 256, src + 1000, sc, None) == zr.ZR_EINVAL     # codes inside src
+    assert L.zr_quantize_int4(src, 1000, 256, q, q + 496, None) == zr.ZR_EINVAL         # scales over the codes' tail
+    assert L.zr_quantize_int4(src, 0, 256, q, sc, None) == zr.ZR_OK
+    assert L.zr_quantize_int4(None, 0, 256, None, None, None) == zr.ZR_OK
+    assert L.zr_dequantize_int4(q, sc, -1, 256, dst, None) == zr.ZR_EINVAL
+    assert L.zr_dequantize_int4(q, sc, 16, 256, None, None) == zr.ZR_EINVAL
+    assert L.zr_dequantize_int4(None, sc, 16, 256, dst, None) == zr.ZR_EINVAL
+    assert L.zr_dequantize_int4(q, sc, 16, 256, dst + 1, None) == zr.ZR_EALIGN
+    assert L.zr_dequantize_int4(q, sc + 1, 16, 256, dst, None) == zr.ZR_EALIGN
+    assert L.zr_dequantize_int4(q, sc, 1000, 256, q - 1000, None) == zr.ZR_EINVAL       # dst over the codes' head
+    assert L.zr_dequantize_int4(q, sc, 0, 256, dst, None) == zr.ZR_OK
+
+
+def test_int4_binding_checks_buffer_sizes():
+    src = torch.zeros(1001, dtype=torch.int16)
+    with pytest.raises(ValueError):   # 1001 codes need 501 bytes
+        zr.zr_quantize_int4(src, torch.zeros(500, dtype=torch.uint8), torch.zeros(4, dtype=torch.float32), block=256)
+    with pytest.raises(ValueError):
+        zr.zr_quantize_int4(src, torch.zeros(501, dtype=torch.uint8), torch.zeros(3, dtype=torch.float32), block=256)
+    with pytest.raises(ValueError):
+        zr.zr_dequantize_int4(torch.zeros(501, dtype=torch.uint8), torch.zeros(1, dtype=torch.float32), src, block=512)
+
+
 def test_int8_binding_checks_buffer_sizes():
     src = torch.zeros(1000, dtype=torch.int16)
     with pytest.raises(ValueError):
@@ -367,14 +402,16 @@ def test_int8_binding_checks_buffer_sizes():
         zr.zr_dequantize_int8(torch.zeros(1000, dtype=torch.int8), torch.zeros(1, dtype=torch.float32), src, block=512)
 
 
-def test_unpack_int8_validation():
+@pytest.mark.parametrize("fn", ["zr_unpack_int8", "zr_unpack_int4"])
+def test_unpack_quantized_validation(fn):
     lay = zr.zr_layout_create([10, 6, 3], 4, 4)  # tensor 2 persistent; psi_pad 16, shard 4
     L = zr._lib
     good = _views((A, 0, 10), (A + 4096, 0, 6), (None, 0, 0))
     q, sc = A + 2**20, A + 2**21
+    code_bytes = 16 if fn == "zr_unpack_int8" else 8   # int4: 2 bytes per shard of 4
 
     def call(layout, qq, ss, block, b, e, views=good, n_views=3):
-        return L.zr_unpack_int8(layout, qq, ss, block, b, e, views, n_views, None)
+        return getattr(L, fn)(layout, qq, ss, block, b, e, views, n_views, None)
 
     assert call(None, q, sc, 256, 0, 16) == zr.ZR_EINVAL
     for block in (0, 128, 300, 4096):
@@ -386,7 +423,7 @@ def test_unpack_int8_validation():
     assert call(lay.handle, None, sc, 256, 0, 16) == zr.ZR_EINVAL
     assert call(lay.handle, q, None, 256, 0, 16) == zr.ZR_EINVAL
     assert call(lay.handle, q, sc + 2, 256, 0, 16) == zr.ZR_EALIGN
-    assert call(lay.handle, q, q + 8, 256, 0, 16) == zr.ZR_EINVAL           # scales inside the codes
+    assert call(lay.handle, q, q + code_bytes - 4, 256, 0, 16) == zr.ZR_EINVAL   # scales over the codes' tail
     assert call(lay.handle, q, sc, 256, 3, 3) == zr.ZR_OK                   # empty range
     assert call(lay.handle, None, None, 256, 3, 3) == zr.ZR_OK
     short = _views((A, 0, 9), (A + 4096, 0, 6), (None, 0, 0))

@@ -5,8 +5,8 @@ buffers.  The full-grid results are checked against the oracle by the other
 GPU tests; here every kernel family runs both ways on the same inputs: AdamW
 (vector and element-wise paths), the reduce (XCD-ordered n <= 8, default order
 n > 8, element-wise), the fused reduce + AdamW, the fp16 mean, finite check and
-AdamW, the int8 quantizer and dequantizer (vector and element-wise), the
-dequantize-on-unpack and the pack/unpack copy kernel."""
+AdamW, the int8 and int4 quantizers and dequantizers (vector and element-wise), the
+dequantize-on-unpack of both and the pack/unpack copy kernel."""
 import numpy as np
 import pytest
 import torch
@@ -142,6 +142,25 @@ def test_int8_codec(monkeypatch, block, off):
     both_ways(monkeypatch, run)
 
 
+@pytest.mark.parametrize("block,off", [(256, 0), (2048, 0), (512, 2)])  # off 2: element-wise kernels
+def test_int4_codec(monkeypatch, block, off):
+    device()
+    n = 900_001
+    x = bf16(n, 0.02, 51)
+    nb = -(-n // block)
+
+    def run():
+        src = Placed(x, off)
+        q = Placed(np.zeros(-(-n // 2), np.uint8), off)
+        sc = Placed(np.zeros(nb, np.float32), 0)
+        zr.zr_quantize_int4(src.view, q.view, sc.view, block=block)
+        back = Placed(np.zeros(n, np.uint16), off)
+        zr.zr_dequantize_int4(q.view, sc.view, back.view, block=block)
+        return outputs([q, sc, back])
+
+    both_ways(monkeypatch, run)
+
+
 def test_copy_and_unpack_int8(monkeypatch):
     dev = device()
     numels = [300_001, 7, 250_013, 123_457, 99_999, 400_003]
@@ -154,6 +173,9 @@ def test_copy_and_unpack_int8(monkeypatch):
     codes = np.random.default_rng(61).integers(-127, 128, psi_pad).astype(np.int8)
     scales = np.abs(np.random.default_rng(62).normal(0, 1e-3, 3 * per_rank)).astype(np.float32)
     persistent = [zr.zr_layout_tensor(lay, t)[0] for t in range(len(numels))]
+    codes4 = np.random.default_rng(63).integers(0, 256, 3 * -(-S // 2)).astype(np.uint8)
+    codes4[(codes4 & 0xF) == 8] ^= 1                     # no -8 codes
+    codes4[(codes4 >> 4) == 8] ^= 0x10
 
     def run():
         views = [None if persistent[t] else Placed(views_host[t], t % 3) for t in range(len(numels))]
@@ -165,6 +187,9 @@ def test_copy_and_unpack_int8(monkeypatch):
         q = torch.from_numpy(codes).to(dev)
         sc = torch.from_numpy(scales).to(dev)
         zr.zr_unpack_int8(lay, q, sc, 0, psi_pad, [None if p is None else p.view for p in deq], block=block)
-        return outputs([flat] + [p for p in back + deq if p is not None])
+        deq4 = [None if persistent[t] else Placed(np.zeros(numels[t], np.uint16), 3) for t in range(len(numels))]
+        q4 = torch.from_numpy(codes4).to(dev)
+        zr.zr_unpack_int4(lay, q4, sc, 0, psi_pad, [None if p is None else p.view for p in deq4], block=block)
+        return outputs([flat] + [p for p in back + deq + deq4 if p is not None])
 
     both_ways(monkeypatch, run)

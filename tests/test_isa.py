@@ -27,7 +27,8 @@ CSRC = os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "csrc")
 #   reduce (8-pointer table, XCD order): two batches of 4 contribution loads.
 #   fused: master/m/v as AdamW, 8 dwordx2 contribution loads, dwordx2 copy.
 #   copy: aligned or funnel-shifted (two) loads, one store per lane.
-#   int8 quantizer: 4 chunks of 16-byte loads per tile, 8-byte code stores.
+#   int8 quantizer: 4 chunks of 16-byte loads per tile, 8-byte code stores
+#   (int4: 4-byte code stores, beside the scale stores of the same width).
 KERNELS = [
     ("adamw.hip", "adamw_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                             "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
@@ -38,7 +39,10 @@ KERNELS = [
                                                "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
     ("copy.hip", "copy_kernel", {"global_load_dwordx4": 2, "global_store_dwordx4": 1}),
     ("unpack_int8.hip", "unpack_int8_kernel", {"global_store_dwordx4": 5}),
-    ("quant.hip", "quantize_vec_kernelILi2048E", {"global_load_dwordx4": 4, "global_store_dwordx2": 4}),
+    ("quant.hip", "quantize_vec_kernelILi2048ELi127E", {"global_load_dwordx4": 4, "global_store_dwordx2": 4}),
+    ("quant.hip", "quantize_vec_kernelILi2048ELi7E", {"global_load_dwordx4": 4}),
+    ("quant.hip", "dequantize_vec_kernelILi2048ELi7E", {"global_store_dwordx4": 4}),
+    ("unpack_int8.hip", "unpack_int4_kernel", {"global_store_dwordx4": 13}),
 ]
 
 

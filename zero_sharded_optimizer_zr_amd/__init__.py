@@ -86,6 +86,9 @@ _SIGS = {
     "zr_quantize_int8": ([_P, _I64, _I32, _P, _P, _P], _I32),
     "zr_dequantize_int8": ([_P, _P, _I64, _I32, _P, _P], _I32),
     "zr_unpack_int8": ([_P, _P, _P, _I32, _I64, _I64, _P, _I32, _P], _I32),
+    "zr_quantize_int4": ([_P, _I64, _I32, _P, _P, _P], _I32),
+    "zr_dequantize_int4": ([_P, _P, _I64, _I32, _P, _P], _I32),
+    "zr_unpack_int4": ([_P, _P, _P, _I32, _I64, _I64, _P, _I32, _P], _I32),
     "zr_host_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _I32], _I32),
     "zr_host_simd": ([], ctypes.c_char_p),
     "zr_offload_adamw_step": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I32, _P], _I32),
@@ -396,6 +399,51 @@ def zr_unpack_int8(layout: Layout, q: torch.Tensor, scales: torch.Tensor, begin:
         g = lambda i: (i // S) * per_rank + (i % S) // int(block)
         _need(g(int(end) - 1) - g(int(begin)) + 1, scales=scales)
     _check(_lib.zr_unpack_int8(layout.handle, _ptr(q, 1, "q"), _ptr(scales, 4, "scales"), int(block), int(begin),
+                               int(end), _views(layout, views), len(views), _stream(stream)))
+
+
+def _int4_sizes(numel: int, block: int, q4: torch.Tensor, scales: torch.Tensor):
+    if q4.numel() * q4.element_size() < -(-numel // 2):
+        raise ValueError(f"q4 holds {q4.numel() * q4.element_size()} bytes, {-(-numel // 2)} needed")
+    if block > 0 and scales.numel() < -(-numel // block):
+        raise ValueError(f"scales holds {scales.numel()} entries, {-(-numel // block)} needed")
+
+
+def zr_quantize_int4(src: torch.Tensor, q4: torch.Tensor, scales: torch.Tensor, block: int = 2048,
+                     numel: Optional[int] = None, stream=None) -> None:
+    """As zr_quantize_int8 with 7 for 127; codes two per byte in q4 (uint8),
+    element 2j in the low four bits of byte j."""
+    numel = src.numel() if numel is None else int(numel)
+    _need(numel, src=src)
+    _int4_sizes(numel, int(block), q4, scales)
+    _check(_lib.zr_quantize_int4(_ptr(src, 2, "src"), numel, int(block), _ptr(q4, 1, "q4"),
+                                 _ptr(scales, 4, "scales"), _stream(stream)))
+
+
+def zr_dequantize_int4(q4: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor, block: int = 2048,
+                       numel: Optional[int] = None, stream=None) -> None:
+    """dst[i] = bf16(code i of q4 * scales[i // block])."""
+    numel = dst.numel() if numel is None else int(numel)
+    _need(numel, dst=dst)
+    _int4_sizes(numel, int(block), q4, scales)
+    _check(_lib.zr_dequantize_int4(_ptr(q4, 1, "q4"), _ptr(scales, 4, "scales"), numel, int(block),
+                                   _ptr(dst, 2, "dst"), _stream(stream)))
+
+
+def zr_unpack_int4(layout: Layout, q4: torch.Tensor, scales: torch.Tensor, begin: int, end: int,
+                   views: Sequence[ViewArg], block: int = 2048, stream=None) -> None:
+    """Per-tensor views <- bf16(code * scale) for flat elements [begin, end) of
+    an int4 quantized AllGather (codes and blocks per shard); q4[0] is the byte
+    holding element begin's code and scales[0] the scale of its block."""
+    if end > begin and int(block) > 0:
+        S = zr_layout_query(layout)["shard"]
+        per_rank, nbytes = -(-S // int(block)), -(-S // 2)
+        g = lambda i: (i // S) * per_rank + (i % S) // int(block)
+        cb = lambda i: (i // S) * nbytes + (i % S) // 2
+        _need(g(int(end) - 1) - g(int(begin)) + 1, scales=scales)
+        if q4.numel() * q4.element_size() < cb(int(end) - 1) - cb(int(begin)) + 1:
+            raise ValueError("q4 is too short for the range")
+    _check(_lib.zr_unpack_int4(layout.handle, _ptr(q4, 1, "q4"), _ptr(scales, 4, "scales"), int(block), int(begin),
                                int(end), _views(layout, views), len(views), _stream(stream)))
 
 
