@@ -139,6 +139,64 @@ def test_captured_fused_and_fp16_paths_with_an_overflow():
     zr.zr_graph_destroy(g)
 
 
+@pytest.mark.parametrize("bits", [8, 4])
+def test_captured_step_with_a_quantized_gather(bits):
+    """A step that ends in the quantized AllGather's local halves -- AdamW, the
+    rank's own shard quantized into its slot of the gathered codes, then the
+    whole gathered range rebuilt into the views -- recorded once and replayed,
+    equal to the eager calls after every replay."""
+    dev = device()
+    w = TINY_MLP
+    block = 256
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    info = zr.zr_layout_query(lay)
+    S, G = info["shard"], info["psi_pad"]
+    per_rank = -(-S // block)
+    nbytes = S if bits == 8 else -(-S // 2)
+    quantize = zr.zr_quantize_int8 if bits == 8 else zr.zr_quantize_int4
+    unpack = zr.zr_unpack_int8 if bits == 8 else zr.zr_unpack_int4
+    ctype = torch.int8 if bits == 8 else torch.uint8
+
+    def buffers(seed):
+        g = synth.normal_bf16(S, 1e-3, seed, dev)
+        st = [x.clone() for x in synth.shard_state(w, S, device=dev).values()]
+        flat = torch.zeros(S, dtype=torch.int16, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(seed)
+        codes = torch.randint(-7, 8, (w.n_d * nbytes,), dtype=torch.int8, device=dev, generator=gen).view(ctype)
+        scales = torch.rand(w.n_d * per_rank, dtype=torch.float32, device=dev, generator=gen) * 1e-3
+        views = [None if zr.zr_layout_tensor(lay, t)[0] else torch.zeros(x, dtype=torch.int16, device=dev)
+                 for t, x in enumerate(w.numels)]
+        return g, st, flat, codes, scales, views
+
+    def calls(bf, step, stream):
+        g, st, flat, codes, scales, views = bf
+        zr.zr_adamw_step(g, *st, flat, step=step, stream=stream, **w.hparams)
+        quantize(flat, codes[:nbytes], scales[:per_rank], block=block, stream=stream)
+        unpack(lay, codes, scales, 0, G, views, block=block, stream=stream)
+
+    eager, rec = buffers(31), buffers(31)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        zr.zr_graph_capture_begin()
+        calls(rec, 1, None)
+        g = zr.zr_graph_capture_end()
+    assert zr.zr_graph_info(g)[1] == 1
+    for t in range(1, 4):
+        say("captured quantized-gather step", bits, t)
+        calls(eager, t, torch.cuda.current_stream())
+        zr.zr_graph_set_adamw(g, step=t, **w.hparams)
+        zr.zr_graph_launch(g, side)
+        torch.cuda.synchronize()
+        for a, b in zip(eager[1] + [eager[2], eager[3].view(torch.int8), eager[4]],
+                        rec[1] + [rec[2], rec[3].view(torch.int8), rec[4]]):
+            assert eq(a, b) if a.dtype != torch.int8 else torch.equal(a, b), f"step {t}"
+        for a, b in zip(eager[5], rec[5]):
+            assert a is None or torch.equal(a, b), f"views, step {t}"
+    zr.zr_graph_destroy(g)
+
+
 @pytest.mark.slow
 def test_captured_gpt_shard_ten_steps_with_fresh_contributions():
     """The GPT-7.5B shard over 64 ranks (116,465,664 elements, 435 tensors),
