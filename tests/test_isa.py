@@ -38,11 +38,11 @@ KERNELS = [
     ("fp16.hip", "adamw_f16_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                                "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
     ("copy.hip", "copy_kernel", {"global_load_dwordx4": 2, "global_store_dwordx4": 1}),
-    ("unpack_int8.hip", "unpack_int8_kernel", {"global_store_dwordx4": 5}),
+    ("unpack_quant.hip", "unpack_int8_kernel", {"global_store_dwordx4": 5}),
     ("quant.hip", "quantize_vec_kernelILi2048ELi127E", {"global_load_dwordx4": 4, "global_store_dwordx2": 4}),
     ("quant.hip", "quantize_vec_kernelILi2048ELi7E", {"global_load_dwordx4": 4}),
     ("quant.hip", "dequantize_vec_kernelILi2048ELi7E", {"global_store_dwordx4": 4}),
-    ("unpack_int8.hip", "unpack_int4_kernel", {"global_store_dwordx4": 13}),
+    ("unpack_quant.hip", "unpack_int4_kernel", {"global_store_dwordx4": 13}),
 ]
 
 
