@@ -11,11 +11,12 @@
  *   4. bit copies between per-tensor bf16 views and the flat buffer
  *                                                    (zr_pack / zr_unpack)
  * and 2 + 3 in one pass (zr_reduce_adamw_step), an fp16 variant of 2 + 3
- * with dynamic loss scaling (zr_*_f16, zr_loss_scale_*), and int8 block
+ * with dynamic loss scaling (zr_*_f16, zr_loss_scale_*), int8 and int4 block
  * quantization of the bf16 shard for a quantized parameter AllGather
- * (zr_quantize_int8 / zr_dequantize_int8 / zr_unpack_int8), and the
- * ZeRO-Offload step with the optimizer on the host (zr_offload_adamw_step,
- * zr_host_adamw_step).
+ * (zr_quantize_int8 / zr_dequantize_int8 / zr_unpack_int8 and the _int4
+ * forms), the ZeRO-Offload step with the optimizer on the host
+ * (zr_offload_adamw_step, zr_host_adamw_step), and captured steps replayed as
+ * HIP graphs (zr_graph_*).
  *
  * Sources are web pages on DeepSpeed ZeRO-3, cited by title and section:
  *   [ENC]  "DeepSpeed ZeRO-3", encyclopedia entry (baike.kuaisou.com)
