@@ -351,7 +351,7 @@ def test_fp16_loss_scaled_step_full_size():
 
 def test_next_kernels_beyond_2_pow_31_elements():
     """64-bit indexing of the fused reduce + AdamW, the fp16 mean and AdamW,
-    the int8 codec and the dequantize-on-unpack over more than 2^31 elements,
+    the int8 and int4 codecs and their dequantize-on-unpack over more than 2^31 elements,
     each checked on sampled elements (or sampled blocks) against the oracle."""
     dev = device()
     n = (1 << 31) + 13
@@ -416,7 +416,27 @@ def test_next_kernels_beyond_2_pow_31_elements():
     zr.zr_unpack_int8(glay, q, sc, 0, n, [out], block=block)
     torch.cuda.synchronize()
     assert torch.equal(out, back)
-    del q, sc, back, out, param
+    del q, sc, back, out
+    torch.cuda.empty_cache()
+    # the int4 codec over the same parameters, and its dequantize-on-unpack
+    q4 = torch.empty(-(-n // 2), dtype=torch.uint8, device=dev)
+    sc4 = torch.empty(nb, dtype=torch.float32, device=dev)
+    back4 = torch.empty(n, dtype=torch.int16, device=dev)
+    zr.zr_quantize_int4(param, q4, sc4, block=block)
+    zr.zr_dequantize_int4(q4, sc4, back4, block=block)
+    torch.cuda.synchronize()
+    for b in np.unique(np.concatenate([rng.integers(0, nb, 300), [nb // 2, nb - 2, nb - 1]])):
+        lo, hi = int(b) * block, min(n, (int(b) + 1) * block)
+        rq, rs = oracle.quantize_int4(param.view(torch.int16)[lo:hi].cpu().numpy().view(np.uint16).copy(), block)
+        assert_bits_equal(sc4[int(b):int(b) + 1].cpu().numpy(), rs, f"int4 scale of block {b}")
+        assert_bits_equal(q4[lo // 2:(hi + 1) // 2].cpu().numpy(), rq, f"int4 codes of block {b}")
+        assert_bits_equal(back4[lo:hi].cpu().numpy().view(np.uint16), oracle.dequantize_int4(rq, rs, hi - lo, block),
+                          f"int4 rebuilt block {b}")
+    out4 = torch.empty(n, dtype=torch.int16, device=dev)
+    zr.zr_unpack_int4(glay, q4, sc4, 0, n, [out4], block=block)
+    torch.cuda.synchronize()
+    assert torch.equal(out4, back4)
+    del q4, sc4, back4, out4, param
     torch.cuda.empty_cache()
 
 
