@@ -444,7 +444,7 @@ def test_next_kernels_beyond_2_pow_31_elements():
 @pytest.mark.parametrize("w", [LLAMA_7B, GPT_7P5B, FLAT_1T], ids=lambda w: w.name)
 def test_next_paths_on_full_size_shards(w):
     """The fused reduce + AdamW (with its bf16 mean output), the fp16 mean and
-    loss-scaled AdamW, and the int8 codes of the updated parameters, on the
+    loss-scaled AdamW, and the int8 and int4 codes of the updated parameters, on the
     rank's full shard of each workload, sampled against the oracle."""
     dev = device()
     lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
@@ -502,5 +502,14 @@ def test_next_paths_on_full_size_shards(w):
         rq, rs = oracle.quantize_int8(param.view(torch.int16)[lo:hi].cpu().numpy().view(np.uint16).copy(), block)
         assert_bits_equal(sc[int(blk):int(blk) + 1].cpu().numpy(), rs, f"{w.name} scale {blk}")
         assert_bits_equal(q[lo:hi].cpu().numpy(), rq, f"{w.name} codes {blk}")
-    del q, sc, param
+    # and as int4 codes, two per byte
+    q4 = torch.empty(-(-n // 2), dtype=torch.uint8, device=dev)
+    zr.zr_quantize_int4(param, q4, sc, block=block)
+    torch.cuda.synchronize()
+    for blk in np.unique(np.concatenate([rng.integers(0, nb, 200), [0, nb - 1]])):
+        lo, hi = int(blk) * block, min(n, (int(blk) + 1) * block)
+        rq, rs = oracle.quantize_int4(param.view(torch.int16)[lo:hi].cpu().numpy().view(np.uint16).copy(), block)
+        assert_bits_equal(sc[int(blk):int(blk) + 1].cpu().numpy(), rs, f"{w.name} int4 scale {blk}")
+        assert_bits_equal(q4[lo // 2:(hi + 1) // 2].cpu().numpy(), rq, f"{w.name} int4 codes {blk}")
+    del q, q4, sc, param
     torch.cuda.empty_cache()
