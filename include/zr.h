@@ -464,7 +464,9 @@ ZR_API const char *zr_host_simd(void);
  * there (e.g. the reduce that produced grad); parameter copies go on a stream
  * the library keeps per device.  The call is synchronous: it returns when the states are updated and
  * every parameter has reached the device (or, on an error, when the copies it
- * enqueued have finished).  Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
+ * enqueued have finished); being synchronous, it cannot be recorded into a
+ * captured step (ZR_EINVAL while `stream` is being captured).  Errors:
+ * ZR_EINVAL, ZR_EALIGN, ZR_EHIP.
  */
 ZR_API zr_status zr_offload_adamw_step(const void *grad, float *master, float *exp_avg, float *exp_avg_sq,
                                        void *param_out, int64_t numel, const zr_adamw_hparams *hp, void *staging,

@@ -99,6 +99,27 @@ def test_offload_follows_the_stream_order_of_the_gradient():
     assert np.array_equal(bits(op), bits(gp))
 
 
+def test_offload_refuses_a_capturing_stream():
+    """The offloaded step waits for its own copies, so a call on a stream that
+    is being captured is rejected before anything is enqueued."""
+    dev = device()
+    n = 4096
+    grad = torch.zeros(n, dtype=torch.int16, device=dev)
+    hs = [torch.zeros(n, dtype=torch.float32) for _ in range(3)]
+    staging = zr.offload_staging(1 << 20)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        zr.zr_graph_capture_begin()
+        with pytest.raises(zr.ZRError) as e:
+            zr.zr_offload_adamw_step(grad, *hs, None, staging, step=1, **HP)
+        zr.zr_reduce_slice([grad.view(torch.bfloat16)], grad.view(torch.bfloat16))   # something to capture
+        g = zr.zr_graph_capture_end()
+    zr.zr_graph_destroy(g)
+    assert e.value.status == zr.ZR_EINVAL and "captured" in str(e.value)
+    assert all(not h.any() for h in hs)
+
+
 @pytest.mark.slow
 def test_offload_full_shard_7b_over_4_ranks():
     """The 1.75e9-element shard of a 7e9-parameter model over 4 ranks: host

@@ -33,6 +33,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstdlib>
@@ -336,10 +337,15 @@ zr_status check_host_buffers(const char *who, const void *grad, const float *mas
 
 // Waits for a HIP event by polling (a copy of one chunk takes a fraction of a
 // millisecond, and a blocking wait's wake-up latency is a sizeable part of
-// that); returns ZR_EHIP with the message on failure.
+// that); returns ZR_EHIP with the message on failure, or when the event has
+// not completed after kWaitLimit (a chunk's copy, queued behind the caller's
+// earlier work, should take far less).
+constexpr std::chrono::seconds kWaitLimit(300);
+
 zr_status wait_event(hipEvent_t e, const char *who)
 {
-    for (;;) {
+    const auto start = std::chrono::steady_clock::now();
+    for (uint32_t spin = 0;; ++spin) {
         const hipError_t err = hipEventQuery(e);
         if (err == hipSuccess)
             return ZR_OK;
@@ -347,6 +353,8 @@ zr_status wait_event(hipEvent_t e, const char *who)
             return fail(ZR_EHIP, "%s: %s", who, hipGetErrorString(err));
         for (int k = 0; k < 64; ++k)
             _mm_pause();
+        if ((spin & 1023) == 1023 && std::chrono::steady_clock::now() - start > kWaitLimit)
+            return fail(ZR_EHIP, "%s: a copy did not complete within %lld s", who, (long long)kWaitLimit.count());
     }
 }
 
@@ -441,6 +449,13 @@ extern "C" zr_status zr_offload_adamw_step(const void *grad, float *master, floa
     }
     if (numel == 0)
         return ZR_OK;
+    // The call waits for its own copies, so it cannot be recorded into a graph.
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &capture) != hipSuccess)
+        return fail(ZR_EHIP, "%s: hipStreamIsCapturing failed", who);
+    if (capture != hipStreamCaptureStatusNone)
+        return fail(ZR_EINVAL, "%s: the stream is being captured; this call is synchronous and cannot be recorded",
+                    who);
 
     const AdamWScalars s = adamw_scalars(*hp);
     hipStream_t str = static_cast<hipStream_t>(stream), up = nullptr;
