@@ -98,6 +98,12 @@ def test_adamw_every_path_gives_the_same_bits():
     (1000, dict(HP, lr=1e-4, weight_decay=0.1), 1.0, 1e-4, 1e-6),
     (4, HP, 0.125, 1e-4, 1e-6),
     (9, dict(lr=1e-3, beta1=0.0, beta2=0.0, eps=1e-6, weight_decay=0.0), 1.0, 1e-4, 1e-6),
+    (3, dict(HP, lr=0.0), 1.0, 1e-4, 1e-6),                                # no update, no decay
+    (10**9, HP, 1.0, 1e-4, 1e-6),                                          # bias corrections at 1
+    (2, dict(HP, beta1=0.999, beta2=0.999999), 1.0, 1e-4, 1e-6),          # long averages
+    (5, HP, -2.0, 1e-4, 1e-6),                                             # negative gradient scale
+    (5, HP, 0.0, 1e-4, 1e-6),                                              # zero gradient scale
+    (7, dict(HP, eps=1.0, weight_decay=1.0), 1.0, 1e-4, 1e-6),            # large eps and decay
 ])
 def test_adamw_hyperparameters(step, hp, scale, m_std, v_high):
     device()
