@@ -13,7 +13,11 @@
 // (four in flight at a time), dwordx4 loads and stores of master, m and v, a
 // dwordx2 store of the copy; non-temporal, one group per lane over a grid that
 // covers the shard, residency capped per contribution count with reserved LDS
-// the kernel never touches.
+// the kernel never touches.  Tiles dealt to the XCDs in runs (as the reduce
+// does), eight elements per lane, and eight or sixteen contribution loads in
+// flight all measured slower on MI355X (same buffers: n = 4 6.12 against
+// 5.87-5.89 TB/s for the XCD order; n = 64 5.80 against 5.49-5.54 for wider
+// batches, 5.25-5.66 for eight elements per lane).
 //
 // Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
 // blog (111qqz.com), "ZeRO-2: why gradients can be sharded too" (after the
