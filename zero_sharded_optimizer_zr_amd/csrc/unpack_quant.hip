@@ -13,9 +13,9 @@
 // split at shard boundaries, into descriptors {codes, destination, scale of the
 // first block, phase in that block, count}, passed by value in batches; every
 // workgroup rebuilds one tile of 4096 elements of one descriptor (two chunks of
-// 8 per lane, 2048 elements apart, each one aligned 16-byte store; two chunks
-// in flight per lane measured 5.9-6.0 TB/s against 5.3 for one, and capping
-// residency only slowed it), found by a binary search over the batch's tile
+// 8 per lane, 2048 elements apart, each one aligned 16-byte store: two chunks
+// in flight per lane beat one by 12-13% and four by 4%, and capping residency
+// only slowed it), found by a binary search over the batch's tile
 // prefix sums; tiles go to the 8 XCDs in contiguous runs (a grid smaller than
 // the tile count loops, every gridDim.x-th tile).  Codes come in as
 // two aligned 8-byte words per lane, funnel-shifted (v_alignbyte) when the
@@ -29,8 +29,8 @@
 // shard is odd, and a lane's 8 codes are 32 bits at a bit offset (8 per byte
 // phase, 4 for the odd nibble) uniform per descriptor, taken from two aligned
 // 4-byte words by a 64-bit shift when the offset is not 0.  Four chunks per
-// lane there (6.02 TB/s against 5.47 for two, on the 7e9 gather; int8 keeps
-// two: 6.44 against 6.20 for four).
+// lane there (6.02 TB/s against 5.47 for two on the 7e9 gather, where half as
+// many code bytes per lane leave the loads too narrow to cover the latency).
 //
 // Reads past a descriptor's last code stay inside the aligned 8-byte (int8) or
 // 4-byte (int4) word that holds that code.
