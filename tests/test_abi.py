@@ -29,6 +29,8 @@ def test_every_declared_symbol_is_exported_and_bound():
     for name in names:
         assert hasattr(lib, name), name
         assert callable(getattr(zr, name)), name
+        assert name in zr.__all__, name
+    assert all(hasattr(zr, name) for name in zr.__all__)
     assert set(names) == set(zr.SYMBOLS)
     assert zr.zr_abi_version() == 1
 

@@ -18,11 +18,14 @@ from typing import List, Optional, Sequence, Tuple, Union
 import torch  # loads the process's HIP runtime before libzr binds to it
 
 __all__ = [
-    "ZRError", "Layout", "zr_layout_create", "zr_layout_destroy", "zr_layout_query", "zr_layout_tensor",
+    "ZRError", "Layout", "Graph", "zr_layout_create", "zr_layout_destroy", "zr_layout_query", "zr_layout_tensor",
     "zr_layout_rank_range", "zr_layout_fragments", "zr_layout_ledger_bytes", "zr_pack", "zr_unpack",
     "zr_reduce_slice", "zr_adamw_step", "zr_reduce_adamw_step", "zr_loss_scale_init", "zr_reduce_slice_f16",
-    "zr_check_finite_f16", "zr_adamw_step_f16", "zr_loss_scale_update", "loss_scale_record", "zr_last_error",
-    "zr_abi_version", "LIBRARY",
+    "zr_check_finite_f16", "zr_adamw_step_f16", "zr_loss_scale_update", "loss_scale_record",
+    "zr_quantize_int8", "zr_dequantize_int8", "zr_unpack_int8", "zr_quantize_int4", "zr_dequantize_int4",
+    "zr_unpack_int4", "zr_host_simd", "zr_host_adamw_step", "offload_staging", "zr_offload_adamw_step",
+    "zr_graph_capture_begin", "zr_graph_capture_end", "zr_graph_info", "zr_graph_set_adamw", "zr_graph_launch",
+    "zr_graph_destroy", "zr_last_error", "zr_abi_version", "LIBRARY", "SYMBOLS",
 ]
 
 LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzr.so")
