@@ -15,7 +15,9 @@
 // 6.06 -> 6.43 TB/s; n = 8 at 4 per CU with the XCD order 5.66 -> 5.99 TB/s
 // (the cap alone gained nothing at n <= 8 in this arrangement); n = 64 at 2 per
 // CU in the default order 5.8 -> 6.1-6.3 TB/s, where the XCD order lost a
-// tenth.  The n device pointers travel by value in the kernel arguments.
+// tenth.  Two 8-element chunks per lane (twice the loads in flight) lost 3-4%
+// at n = 4 and n = 8 at every cap from 3 to 5 workgroups per CU.  The n device
+// pointers travel by value in the kernel arguments.
 //
 // Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
 // blog (111qqz.com), "ZeRO-2: why gradients can be sharded too" (ReduceScatter
