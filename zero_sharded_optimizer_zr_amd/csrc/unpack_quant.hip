@@ -32,6 +32,12 @@
 // lane there (6.02 TB/s against 5.47 for two on the 7e9 gather, where half as
 // many code bytes per lane leave the loads too narrow to cover the latency).
 //
+// Measured equal or slower on MI355X, same buffers: the packed hardware bf16
+// conversion (half the vector ALU work), one scale per lane where no lane's 8
+// elements can straddle two blocks (int8 -1%), the wave's scales fetched once
+// with scalar loads (int8 +1%, int4 -10%), fewer chunks per lane with either
+// (int8 one chunk -11%, int4 two -10%), and a residency cap for int4 (-6%).
+//
 // Reads past a descriptor's last code stay inside the aligned 8-byte (int8) or
 // 4-byte (int4) word that holds that code.
 //
