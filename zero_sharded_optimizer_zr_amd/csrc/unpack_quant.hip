@@ -31,6 +31,11 @@
 // 4-byte words by a 64-bit shift when the offset is not 0.  Four chunks per
 // lane there (6.02 TB/s against 5.47 for two on the 7e9 gather, where half as
 // many code bytes per lane leave the loads too narrow to cover the latency).
+// The int4 code loads are ordinary cached loads: with the non-temporal hint
+// these 4-byte-per-lane loads fetched 4.3% more than the code bytes from HBM
+// (FETCH_SIZE), and ran 1% slower; cached, the fetch equals the code and scale
+// bytes.  (The int8 code loads, 8 bytes per lane, fetch exactly their bytes
+// either way and keep the hint.)
 //
 // Measured equal or slower on MI355X, same buffers: the packed hardware bf16
 // conversion (half the vector ALU work), one scale per lane where no lane's 8
@@ -165,9 +170,9 @@ __device__ __forceinline__ void rebuild_chunks4(const uint32_t *s1, uint32_t shi
     for (int k = 0; k < kPerLane4; ++k) {
         const int64_t c = c0 + k * kBlock;
         if (kFull || c < body) {
-            w[k] = load_stream(s1 + c);
+            w[k] = load_global(s1 + c);  // cached: see the header
             if (kShift)
-                w2[k] = load_stream(s1 + c + 1);
+                w2[k] = load_global(s1 + c + 1);
             const int64_t e0 = e_base + 8 * c;
             const int64_t j0 = e0 >> lg;
             sa[k] = load_global(scale + j0);
