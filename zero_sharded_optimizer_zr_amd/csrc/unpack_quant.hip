@@ -3,8 +3,8 @@
 // elements [begin, end) of the partition, one int8 code per element and one
 // fp32 scale per block; blocks are those of the ranks that quantized their own
 // shards (zr_quantize_int8 on elements [r S, (r+1) S)), so the block grid
-// restarts at every shard and a
-// shard's last block is short when the block size does not divide S.  Every
+// restarts at every shard and a shard's last block is short when the block
+// size does not divide S.  Every
 // element is rebuilt as bf16(code * scale) and written straight into its
 // tensor view: 1 byte read and 2 bytes written per element, where dequantizing
 // into a flat bf16 buffer and unpacking that would move 7.
