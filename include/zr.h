@@ -136,14 +136,25 @@ typedef struct zr_adamw_hparams {
 ZR_API zr_status zr_layout_create(const int64_t *numels, int32_t n_tensors, int32_t n_d,
                            int64_t persist_threshold, zr_layout **out);
 
-/* Free a layout; NULL is ignored. */
+/* Free a layout and the host memory it owns; NULL is ignored.  The layout is
+ * the host-side record of the partition that zr_layout_create describes
+ * ([TUT] 2.1); no device memory is involved. */
 ZR_API void zr_layout_destroy(zr_layout *layout);
 
-/* Sizes and counts of a layout.  Errors: ZR_EINVAL (NULL). */
+/* Sizes and counts of a layout: psi and its split into partitioned and
+ * persistent elements ([ART] small-parameter residency paragraph: tensors
+ * under the threshold stay whole on every rank), the padded flat length and
+ * the per-rank slice ([TUT] 2.1: each rank owns 1/N_d of the flat buffer;
+ * [ENC] Principle: each rank keeps 1/N_d of parameters, gradients and
+ * optimizer state).  Errors: ZR_EINVAL (NULL). */
 ZR_API zr_status zr_layout_query(const zr_layout *layout, zr_layout_info *out);
 
 /* Tensor t: *persistent = 1 if replicated, and *offset = its offset in the
  * persistent region; else *persistent = 0 and *offset = its flat offset.
+ * [ART] small-parameter residency paragraph (tensors under
+ * stage3_param_persistence_threshold are kept whole on every rank rather than
+ * partitioned) and minimal ZeRO-3 config (threshold 100000); [TUT] 3.2
+ * (partitioned tensors live in one contiguous buffer, in list order).
  * Either output pointer may be NULL.  Errors: ZR_EINVAL, ZR_ERANGE (t). */
 ZR_API zr_status zr_layout_tensor(const zr_layout *layout, int32_t t, int32_t *persistent, int64_t *offset);
 

@@ -262,6 +262,51 @@ def test_binding_rejects_bad_tensors():
                      stream=0)
 
 
+def test_binding_rejects_host_tensors_for_kernels():
+    """Every wrapper of a GPU kernel refuses host (CPU) tensors of the right
+    size and dtype with ValueError before the library is called, so a host
+    address never reaches a kernel; the host AdamW refuses GPU-side roles the
+    same way (no GPU is touched: every case fails in the binding)."""
+    i16 = lambda n: torch.zeros(n, dtype=torch.int16)
+    f32 = lambda n: torch.zeros(n, dtype=torch.float32)
+    ls = torch.zeros(4, dtype=torch.int32)
+    hp = dict(lr=5e-5, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
+    lay = zr.zr_layout_create([300_000, 200_000], 4)
+    views = [i16(300_000), i16(200_000)]
+    cases = {
+        "pack": lambda: zr.zr_pack(lay, views, i16(100), 0, 100),
+        "unpack": lambda: zr.zr_unpack(lay, i16(100), 0, 100, views),
+        "reduce": lambda: zr.zr_reduce_slice([i16(100), i16(100)], i16(100)),
+        "adamw": lambda: zr.zr_adamw_step(i16(100), f32(100), f32(100), f32(100), i16(100), **hp),
+        "adamw no copy": lambda: zr.zr_adamw_step(i16(100), f32(100), f32(100), f32(100), None, **hp),
+        "fused": lambda: zr.zr_reduce_adamw_step([i16(100)], f32(100), f32(100), f32(100), None, i16(100), **hp),
+        "ls init": lambda: zr.zr_loss_scale_init(ls),
+        "reduce f16": lambda: zr.zr_reduce_slice_f16([i16(100)], i16(100), ls),
+        "check f16": lambda: zr.zr_check_finite_f16(i16(100), ls),
+        "adamw f16": lambda: zr.zr_adamw_step_f16(i16(100), f32(100), f32(100), f32(100), None, ls, **hp),
+        "ls update": lambda: zr.zr_loss_scale_update(ls),
+        "quantize int8": lambda: zr.zr_quantize_int8(i16(100), torch.zeros(100, dtype=torch.int8), f32(1),
+                                                     block=256),
+        "dequantize int8": lambda: zr.zr_dequantize_int8(torch.zeros(100, dtype=torch.int8), f32(1), i16(100),
+                                                         block=256),
+        "unpack int8": lambda: zr.zr_unpack_int8(lay, torch.zeros(1000, dtype=torch.int8), f32(4), 0, 1000, views,
+                                                 block=256),
+        "quantize int4": lambda: zr.zr_quantize_int4(i16(100), torch.zeros(50, dtype=torch.uint8), f32(1),
+                                                     block=256),
+        "dequantize int4": lambda: zr.zr_dequantize_int4(torch.zeros(50, dtype=torch.uint8), f32(1), i16(100),
+                                                         block=256),
+        "unpack int4": lambda: zr.zr_unpack_int4(lay, torch.zeros(500, dtype=torch.uint8), f32(4), 0, 1000, views,
+                                                 block=256),
+    }
+    for name, call in cases.items():
+        with pytest.raises(ValueError, match="must be a cuda tensor"):
+            call()
+    # the offload step's gradient and parameters are device buffers
+    staging = torch.zeros(1 << 16, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        zr.zr_offload_adamw_step(i16(100), f32(100), f32(100), f32(100), i16(100), staging, **hp)
+
+
 @pytest.mark.parametrize("case,table,n,outs,numel,hp,code", [
     ("null hp", "t2", 2, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, None, zr.ZR_EINVAL),
     ("null table", None, 2, (A, A + 2**24, A + 2**25, A + 2**26, None), 16, "hp", zr.ZR_EINVAL),

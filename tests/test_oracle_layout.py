@@ -189,3 +189,46 @@ def test_large_offsets_are_exact():
     # the shard starts inside one tensor and ends inside another
     first, last = frs[0], frs[-1]
     assert first[1] > 0 and last[1] + last[3] < llama.numels[last[0]]
+
+
+def test_llama_rank17_fragments_exact():
+    """The Llama-style 7B list over 64 ranks, worked out by hand from its
+    dimensions (hidden 4096, FFN 11008, vocab 32000, 32 layers; HF
+    registration order: embed, then per layer q, k, v, o, gate, up, down and
+    two 4096-element norms, then the final norm and the untied head).  The
+    norms (4096 < 1e5) are persistent; a tensor may straddle rank edges (blog
+    111qqz.com, "ZeRO-3: why parameters can be sharded too": one layer's
+    parameters split over GPUs; tutorial cnhsyj.com 2.1: rank r owns the r-th
+    contiguous 1/N_d of the flat buffer).
+
+    By hand: embed = 32000*4096 = 131,072,000; one layer's partitioned
+    tensors = 4*4096^2 + 3*11008*4096 = 202,375,168; Psi_part = 131,072,000 +
+    32*202,375,168 + 131,072,000 = 6,738,149,376, which 64 divides, so
+    S = 105,283,584 and rank 17 owns [1,789,820,928, 1,895,104,512).  Layer 8
+    starts at 131,072,000 + 8*202,375,168 = 1,750,073,344 (tensor 1 + 9*8 =
+    73 is its q): v (74 + 1 = tensor 75) starts at 1,783,627,776, so the shard
+    begins 6,193,152 elements into v; o (76) and gate (77) lie inside; up (78)
+    starts at 1,862,270,976 and is cut after 32,833,536 of its 45,088,768."""
+    from zr_workloads import LLAMA_7B
+    lay = Layout(LLAMA_7B.numels, LLAMA_7B.n_d, 100_000)
+    assert lay.rank_range(17) == (1_789_820_928, 1_895_104_512)
+    assert lay.fragments(*lay.rank_range(17)) == [
+        (75, 6_193_152, 1_789_820_928, 10_584_064),
+        (76, 0, 1_800_404_992, 16_777_216),
+        (77, 0, 1_817_182_208, 45_088_768),
+        (78, 0, 1_862_270_976, 32_833_536),
+    ]
+    # the whole buffer: one fragment per partitioned tensor (291 - 65 norms)
+    full = lay.fragments(0, lay.psi_pad)
+    assert len(full) == 226 and all(f[1] == 0 and f[3] == lay.numels[f[0]] for f in full)
+    # over all 64 ranks: of the 63 interior rank edges, 62 fall strictly
+    # inside a tensor and cut it into two partial fragments (edge 32, at
+    # 32*S = 3,369,074,688 = 131,072,000 + 16*202,375,168, is the start of
+    # layer 16's q), so 124 fragments are partial; no rank holds more than 6
+    assert 32 * lay.shard == 131_072_000 + 16 * 202_375_168
+    partial, most = 0, 0
+    for r in range(lay.n_d):
+        frs = lay.fragments(*lay.rank_range(r))
+        most = max(most, len(frs))
+        partial += sum(1 for t, toff, _, n in frs if toff > 0 or n < lay.numels[t])
+    assert (partial, most) == (124, 6)

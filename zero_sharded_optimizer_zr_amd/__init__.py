@@ -7,7 +7,9 @@ library's HIP kernels.  PyTorch provides device memory (``torch.Tensor``) and
 streams.  Importing fails loudly if ``libzr.so`` has not been built.
 
 bf16 buffers may be any 2-byte dtype (torch.bfloat16, torch.int16, ...); their
-bits are passed through unchanged.
+bits are passed through unchanged.  Every wrapper of a GPU kernel checks,
+before the library is called, that its buffers are GPU tensors on the device
+of the stream it enqueues on (ValueError otherwise).
 """
 from __future__ import annotations
 
@@ -133,7 +135,10 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
-def _ptr(t: Optional[torch.Tensor], size: int, name: str) -> Optional[int]:
+def _ptr(t: Optional[torch.Tensor], size: int, name: str, device: Optional[str] = None) -> Optional[int]:
+    """Address of a contiguous tensor of `size`-byte elements; with `device`
+    given, the tensor must also live there ("cpu" for the host AdamW's
+    buffers).  The buffers of GPU kernels are checked by _gpu_call."""
     if t is None:
         return None
     if not isinstance(t, torch.Tensor):
@@ -142,7 +147,49 @@ def _ptr(t: Optional[torch.Tensor], size: int, name: str) -> Optional[int]:
         raise TypeError(f"{name} must have {size}-byte elements")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device.type != device:
+        raise ValueError(f"{name} must be a {device} tensor, not one on {t.device}")
     return t.data_ptr() or None
+
+
+def _one_gpu(stream, *tensors) -> None:
+    """Every tensor among `tensors` (None skipped, lists of tensors or of
+    (tensor, first) views flattened) must be a GPU tensor, and all of them on
+    one device, the device of the stream the call is enqueued on (torch's
+    current device when `stream` is None; a raw stream handle is taken to
+    belong to that device).  A host address reaching a kernel would be a GPU
+    memory fault, so it raises here, before the library is called."""
+    flat = []
+    for t in tensors:
+        if isinstance(t, (list, tuple)):
+            flat.extend(x[0] if isinstance(x, tuple) else x for x in t)
+        else:
+            flat.append(t)
+    flat = [t for t in flat if isinstance(t, torch.Tensor)]
+    for t in flat:
+        if t.device.type != "cuda":
+            raise ValueError(f"every buffer of a GPU kernel must be a cuda tensor, not one on {t.device}")
+    devs = {t.device.index for t in flat}
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several GPUs {sorted(devs)}: one call runs on one device")
+    if not devs:
+        return
+    if isinstance(stream, torch.cuda.Stream):
+        want = stream.device.index
+    elif stream is None:
+        want = torch.cuda.current_device()
+    else:
+        return
+    if want not in devs:
+        raise ValueError(f"tensors on cuda:{devs.pop()} but the stream is on cuda:{want}")
+
+
+def _gpu_call(fn, stream, tensors, *args) -> None:
+    """fn(*args, stream) after _one_gpu(stream, *tensors).  The caller has
+    marshalled the arguments (checking sizes and dtypes) before the device
+    check runs; the stream handle is resolved after it."""
+    _one_gpu(stream, *tensors)
+    _check(fn(*args, _stream(stream)))
 
 
 def _need(n: int, **tensors):
@@ -245,16 +292,16 @@ def zr_pack(layout: Layout, views: Sequence[ViewArg], flat: torch.Tensor, begin:
     """flat (holding flat elements [begin, end)) <- per-tensor views; padding zeroed.
     views[t] is None, a tensor holding all of tensor t, or (tensor, first)."""
     _need(int(end) - int(begin), flat=flat)
-    _check(_lib.zr_pack(layout.handle, _views(layout, views), len(views), _ptr(flat, 2, "flat"),
-                        int(begin), int(end), _stream(stream)))
+    _gpu_call(_lib.zr_pack, stream, (flat, views), layout.handle, _views(layout, views), len(views),
+              _ptr(flat, 2, "flat"), int(begin), int(end))
 
 
 def zr_unpack(layout: Layout, flat: torch.Tensor, begin: int, end: int, views: Sequence[ViewArg],
               stream=None) -> None:
     """per-tensor views <- flat elements [begin, end)."""
     _need(int(end) - int(begin), flat=flat)
-    _check(_lib.zr_unpack(layout.handle, _ptr(flat, 2, "flat"), int(begin), int(end),
-                          _views(layout, views), len(views), _stream(stream)))
+    _gpu_call(_lib.zr_unpack, stream, (flat, views), layout.handle, _ptr(flat, 2, "flat"), int(begin), int(end),
+              _views(layout, views), len(views))
 
 
 # ------------------------------------------------------------ reduce/adamw ----
@@ -266,7 +313,7 @@ def zr_reduce_slice(contribs: Sequence[torch.Tensor], out: torch.Tensor, numel: 
     table = (ctypes.c_void_p * max(1, n))(*[_ptr(c, 2, f"contribs[{k}]") for k, c in enumerate(contribs)])
     numel = out.numel() if numel is None else int(numel)
     _need(numel, out=out, **{f"contribs[{k}]": c for k, c in enumerate(contribs)})
-    _check(_lib.zr_reduce_slice(table, n, numel, _ptr(out, 2, "out"), _stream(stream)))
+    _gpu_call(_lib.zr_reduce_slice, stream, (out, contribs), table, n, numel, _ptr(out, 2, "out"))
 
 
 def zr_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
@@ -279,9 +326,9 @@ def zr_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tenso
                   int(step))
     numel = master.numel() if numel is None else int(numel)
     _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
-    _check(_lib.zr_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
-                              _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
-                              ctypes.byref(hp), _stream(stream)))
+    _gpu_call(_lib.zr_adamw_step, stream, (grad, master, exp_avg, exp_avg_sq, param_out), _ptr(grad, 2, "grad"),
+              _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"), _ptr(exp_avg_sq, 4, "exp_avg_sq"),
+              _ptr(param_out, 2, "param_out"), numel, ctypes.byref(hp))
 
 
 def zr_reduce_adamw_step(contribs: Sequence[torch.Tensor], master: torch.Tensor, exp_avg: torch.Tensor,
@@ -298,9 +345,9 @@ def zr_reduce_adamw_step(contribs: Sequence[torch.Tensor], master: torch.Tensor,
     numel = master.numel() if numel is None else int(numel)
     _need(numel, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out, grad_out=grad_out,
           **{f"contribs[{k}]": c for k, c in enumerate(contribs)})
-    _check(_lib.zr_reduce_adamw_step(table, n, _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
-                                     _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"),
-                                     _ptr(grad_out, 2, "grad_out"), numel, ctypes.byref(hp), _stream(stream)))
+    _gpu_call(_lib.zr_reduce_adamw_step, stream, (master, exp_avg, exp_avg_sq, param_out, grad_out, contribs),
+              table, n, _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"), _ptr(exp_avg_sq, 4, "exp_avg_sq"),
+              _ptr(param_out, 2, "param_out"), _ptr(grad_out, 2, "grad_out"), numel, ctypes.byref(hp))
 
 
 # ------------------------------------------------------ fp16 + loss scale ----
@@ -321,7 +368,7 @@ def _ls(ls: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def zr_loss_scale_init(ls: torch.Tensor, initial_scale: float = 2.0 ** 16, stream=None) -> None:
-    _check(_lib.zr_loss_scale_init(_ls(ls), float(initial_scale), _stream(stream)))
+    _gpu_call(_lib.zr_loss_scale_init, stream, (ls,), _ls(ls), float(initial_scale))
 
 
 def zr_reduce_slice_f16(contribs: Sequence[torch.Tensor], out: torch.Tensor, ls: Optional[torch.Tensor] = None,
@@ -331,13 +378,13 @@ def zr_reduce_slice_f16(contribs: Sequence[torch.Tensor], out: torch.Tensor, ls:
     table = (ctypes.c_void_p * max(1, n))(*[_ptr(c, 2, f"contribs[{k}]") for k, c in enumerate(contribs)])
     numel = out.numel() if numel is None else int(numel)
     _need(numel, out=out, **{f"contribs[{k}]": c for k, c in enumerate(contribs)})
-    _check(_lib.zr_reduce_slice_f16(table, n, numel, _ptr(out, 2, "out"), _ls(ls), _stream(stream)))
+    _gpu_call(_lib.zr_reduce_slice_f16, stream, (out, ls, contribs), table, n, numel, _ptr(out, 2, "out"), _ls(ls))
 
 
 def zr_check_finite_f16(grad: torch.Tensor, ls: torch.Tensor, numel: Optional[int] = None, stream=None) -> None:
     numel = grad.numel() if numel is None else int(numel)
     _need(numel, grad=grad)
-    _check(_lib.zr_check_finite_f16(_ptr(grad, 2, "grad"), numel, _ls(ls), _stream(stream)))
+    _gpu_call(_lib.zr_check_finite_f16, stream, (grad, ls), _ptr(grad, 2, "grad"), numel, _ls(ls))
 
 
 def zr_adamw_step_f16(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.Tensor, exp_avg_sq: torch.Tensor,
@@ -350,14 +397,14 @@ def zr_adamw_step_f16(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.T
                   int(step))
     numel = master.numel() if numel is None else int(numel)
     _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
-    _check(_lib.zr_adamw_step_f16(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
-                                  _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
-                                  ctypes.byref(hp), _ls(ls), _stream(stream)))
+    _gpu_call(_lib.zr_adamw_step_f16, stream, (grad, master, exp_avg, exp_avg_sq, param_out, ls),
+              _ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
+              _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel, ctypes.byref(hp), _ls(ls))
 
 
 def zr_loss_scale_update(ls: torch.Tensor, window: int = 1000, factor: float = 2.0, min_scale: float = 1.0,
                          stream=None) -> None:
-    _check(_lib.zr_loss_scale_update(_ls(ls), int(window), float(factor), float(min_scale), _stream(stream)))
+    _gpu_call(_lib.zr_loss_scale_update, stream, (ls,), _ls(ls), int(window), float(factor), float(min_scale))
 
 
 # ---------------------------------------------------------- int8 gather ----
@@ -376,8 +423,8 @@ def zr_quantize_int8(src: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, b
     numel = src.numel() if numel is None else int(numel)
     _need(numel, src=src)
     _int8_sizes(numel, int(block), q, scales)
-    _check(_lib.zr_quantize_int8(_ptr(src, 2, "src"), numel, int(block), _ptr(q, 1, "q"),
-                                 _ptr(scales, 4, "scales"), _stream(stream)))
+    _gpu_call(_lib.zr_quantize_int8, stream, (src, q, scales), _ptr(src, 2, "src"), numel, int(block),
+              _ptr(q, 1, "q"), _ptr(scales, 4, "scales"))
 
 
 def zr_dequantize_int8(q: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor, block: int = 2048,
@@ -386,8 +433,8 @@ def zr_dequantize_int8(q: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor,
     numel = dst.numel() if numel is None else int(numel)
     _need(numel, dst=dst)
     _int8_sizes(numel, int(block), q, scales)
-    _check(_lib.zr_dequantize_int8(_ptr(q, 1, "q"), _ptr(scales, 4, "scales"), numel, int(block),
-                                   _ptr(dst, 2, "dst"), _stream(stream)))
+    _gpu_call(_lib.zr_dequantize_int8, stream, (q, scales, dst), _ptr(q, 1, "q"), _ptr(scales, 4, "scales"), numel,
+              int(block), _ptr(dst, 2, "dst"))
 
 
 def zr_unpack_int8(layout: Layout, q: torch.Tensor, scales: torch.Tensor, begin: int, end: int,
@@ -401,8 +448,8 @@ def zr_unpack_int8(layout: Layout, q: torch.Tensor, scales: torch.Tensor, begin:
         per_rank = -(-S // int(block))
         g = lambda i: (i // S) * per_rank + (i % S) // int(block)
         _need(g(int(end) - 1) - g(int(begin)) + 1, scales=scales)
-    _check(_lib.zr_unpack_int8(layout.handle, _ptr(q, 1, "q"), _ptr(scales, 4, "scales"), int(block), int(begin),
-                               int(end), _views(layout, views), len(views), _stream(stream)))
+    _gpu_call(_lib.zr_unpack_int8, stream, (q, scales, views), layout.handle, _ptr(q, 1, "q"),
+              _ptr(scales, 4, "scales"), int(block), int(begin), int(end), _views(layout, views), len(views))
 
 
 def _int4_sizes(numel: int, block: int, q4: torch.Tensor, scales: torch.Tensor):
@@ -419,8 +466,8 @@ def zr_quantize_int4(src: torch.Tensor, q4: torch.Tensor, scales: torch.Tensor, 
     numel = src.numel() if numel is None else int(numel)
     _need(numel, src=src)
     _int4_sizes(numel, int(block), q4, scales)
-    _check(_lib.zr_quantize_int4(_ptr(src, 2, "src"), numel, int(block), _ptr(q4, 1, "q4"),
-                                 _ptr(scales, 4, "scales"), _stream(stream)))
+    _gpu_call(_lib.zr_quantize_int4, stream, (src, q4, scales), _ptr(src, 2, "src"), numel, int(block),
+              _ptr(q4, 1, "q4"), _ptr(scales, 4, "scales"))
 
 
 def zr_dequantize_int4(q4: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor, block: int = 2048,
@@ -429,8 +476,8 @@ def zr_dequantize_int4(q4: torch.Tensor, scales: torch.Tensor, dst: torch.Tensor
     numel = dst.numel() if numel is None else int(numel)
     _need(numel, dst=dst)
     _int4_sizes(numel, int(block), q4, scales)
-    _check(_lib.zr_dequantize_int4(_ptr(q4, 1, "q4"), _ptr(scales, 4, "scales"), numel, int(block),
-                                   _ptr(dst, 2, "dst"), _stream(stream)))
+    _gpu_call(_lib.zr_dequantize_int4, stream, (q4, scales, dst), _ptr(q4, 1, "q4"), _ptr(scales, 4, "scales"), numel,
+              int(block), _ptr(dst, 2, "dst"))
 
 
 def zr_unpack_int4(layout: Layout, q4: torch.Tensor, scales: torch.Tensor, begin: int, end: int,
@@ -446,8 +493,8 @@ def zr_unpack_int4(layout: Layout, q4: torch.Tensor, scales: torch.Tensor, begin
         _need(g(int(end) - 1) - g(int(begin)) + 1, scales=scales)
         if q4.numel() * q4.element_size() < cb(int(end) - 1) - cb(int(begin)) + 1:
             raise ValueError("q4 is too short for the range")
-    _check(_lib.zr_unpack_int4(layout.handle, _ptr(q4, 1, "q4"), _ptr(scales, 4, "scales"), int(block), int(begin),
-                               int(end), _views(layout, views), len(views), _stream(stream)))
+    _gpu_call(_lib.zr_unpack_int4, stream, (q4, scales, views), layout.handle, _ptr(q4, 1, "q4"),
+              _ptr(scales, 4, "scales"), int(block), int(begin), int(end), _views(layout, views), len(views))
 
 
 # ------------------------------------------------------------ ZeRO-Offload ----
@@ -477,9 +524,9 @@ def zr_host_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: torch.
                   int(step))
     numel = master.numel() if numel is None else int(numel)
     _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
-    _check(_lib.zr_host_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
-                                   _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
-                                   ctypes.byref(hp), int(threads)))
+    _check(_lib.zr_host_adamw_step(_ptr(grad, 2, "grad", "cpu"), _ptr(master, 4, "master", "cpu"),
+                                   _ptr(exp_avg, 4, "exp_avg", "cpu"), _ptr(exp_avg_sq, 4, "exp_avg_sq", "cpu"),
+                                   _ptr(param_out, 2, "param_out", "cpu"), numel, ctypes.byref(hp), int(threads)))
 
 
 def offload_staging(nbytes: int = 64 << 20) -> torch.Tensor:
@@ -504,10 +551,10 @@ def zr_offload_adamw_step(grad: torch.Tensor, master: torch.Tensor, exp_avg: tor
                   int(step))
     numel = master.numel() if numel is None else int(numel)
     _need(numel, grad=grad, master=master, exp_avg=exp_avg, exp_avg_sq=exp_avg_sq, param_out=param_out)
-    _check(_lib.zr_offload_adamw_step(_ptr(grad, 2, "grad"), _ptr(master, 4, "master"), _ptr(exp_avg, 4, "exp_avg"),
-                                      _ptr(exp_avg_sq, 4, "exp_avg_sq"), _ptr(param_out, 2, "param_out"), numel,
-                                      ctypes.byref(hp), _ptr(staging, 1, "staging"), staging.numel(), int(threads),
-                                      _stream(stream)))
+    _gpu_call(_lib.zr_offload_adamw_step, stream, (grad, param_out), _ptr(grad, 2, "grad"),
+              _ptr(master, 4, "master", "cpu"), _ptr(exp_avg, 4, "exp_avg", "cpu"),
+              _ptr(exp_avg_sq, 4, "exp_avg_sq", "cpu"), _ptr(param_out, 2, "param_out"), numel, ctypes.byref(hp),
+              _ptr(staging, 1, "staging", "cpu"), staging.numel(), int(threads))
 
 
 # ---------------------------------------------------------- captured steps ----
