@@ -13,8 +13,10 @@ already resident in HBM when the timed region starts.
 Prints ONE JSON line.  `value` is shard elements per second of the whole step;
 `roofline` is the fused AdamW kernel's algorithmic HBM bandwidth (28 bytes per
 element) from HIP events around each of its launches, against the 8 TB/s
-MI355X peak (and, as a second figure, against the library's copy kernel moving
-the fp32 master in the same run); `cpu_baseline` is the oracle, as it stands,
+MI355X peak (and, as second figures, against the library's copy kernel moving
+the fp32 master and against the AdamW kernel's own access pattern without its
+arithmetic, both in the same run on the same buffers); `cpu_baseline` is the
+oracle, as it stands,
 timed on the host cores over a bounded prefix of the same shard.
 """
 import argparse
@@ -201,6 +203,12 @@ def main():
     elapsed = time.perf_counter() - start
     print(f"[bench] {args.steps} steps in {elapsed:.3f} s", file=sys.stderr, flush=True)
 
+    # the AdamW kernel's access pattern with its arithmetic taken out, on the same
+    # buffers, launched like the AdamW kernel: the bandwidth those eight streams
+    # reach on this placement (master, m and v keep their values; the copy slot
+    # receives the gradient bits and is rewritten by every later step)
+    pattern_ms = pattern_ceiling(grad, master, m, v, flat_param, S, args, stream)
+
     # the same step with the gradient mean and AdamW fused into one pass
     fused_events = {k: [] for k in ("pack", "reduce_adamw", "unpack")}
 
@@ -300,7 +308,14 @@ def main():
                      "traffic": traffic, "algorithmic_bytes_per_launch": bytes_per["adamw"],
                      "bytes_per_element": 28, "elements_per_s": S / (adamw_ms * 1e-3),
                      "copy_ceiling": round(copy_gbps, 1),
-                     "frac_of_copy_ceiling": round(achieved / copy_gbps, 4)},
+                     "frac_of_copy_ceiling": round(achieved / copy_gbps, 4),
+                     "pattern_ceiling": {
+                         "kernel": "zr_measure_adamw_pattern: the AdamW kernel's 4 loads and 4 stores per lane, "
+                                   "launch shape and 5-per-CU cap, without its arithmetic, on the same buffers",
+                         "ms_avg": round(pattern_ms, 4),
+                         "GBps": round(bytes_per["adamw"] / (pattern_ms * 1e-3) / 1e9, 1),
+                         "frac": round(bytes_per["adamw"] / (pattern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "adamw_over_pattern": round(pattern_ms / adamw_ms, 4)}},
         "kernels": kernels,
         "fused_path": {"path": "pack+reduce_adamw+unpack", "ms_per_step": round(fms, 4),
                        "value": S / (fms * 1e-3), "unit": "elements/s",
@@ -320,6 +335,32 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, lay, frags, b, min(args.cpu_sample, S), own_grad, contribs,
                                               st, hp, t_step, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def pattern_ceiling(grad, master, m, v, flat_param, S, args, stream):
+    """Average duration (ms) of the AdamW access-pattern kernel over `steps`
+    launches after `warmup`, HIP events on the launch stream."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "libzr_measure.so"))
+    fn = lib.zr_measure_adamw_pattern
+    fn.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    ptrs = [t.data_ptr() for t in (grad, master, m, v, flat_param)]
+    evs = []
+    for r in range(args.warmup + args.steps):
+        x, y = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        x.record(stream)
+        if fn(*ptrs, S, stream.cuda_stream) != 0:
+            raise RuntimeError("zr_measure_adamw_pattern rejected the buffers")
+        y.record(stream)
+        if r >= args.warmup:
+            evs.append((x, y))
+    torch.cuda.synchronize()
+    return float(np.mean([x.elapsed_time(y) for x, y in evs]))
 
 
 def graph_leg(lay, own_grad, contribs, grad, master, m, v, flat_param, params, b, e, S, hp, t_step, args):

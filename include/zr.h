@@ -271,7 +271,12 @@ ZR_API zr_status zr_adamw_step(const void *grad, float *master, float *exp_avg, 
  * mean of the n bf16 gradient contributions is formed in fp32 (ascending k,
  * one division by n), rounded to bf16, and used at once as the gradient of the
  * AdamW update, without the bf16 gradient's round trip through memory.  Every
- * output is bit for bit what the two calls in sequence produce.  After the
+ * output is bit for bit what the two calls in sequence produce.  Above 24
+ * contributions, where the one-pass kernel's concurrent streams cost more DRAM
+ * efficiency than the mean's round trip saves, the call runs the two kernels
+ * one after the other with the mean in grad_out or, without grad_out, in
+ * param_out (which then receives the copy); with neither output the one-pass
+ * kernel runs at any n.  After the
  * ReduceScatter each rank updates its parameter shard with its gradient shard
  * ([BLOG] "ZeRO-2: why gradients can be sharded too" and "ZeRO-1: why optimizer
  * states can be sharded"; [CON] Stage 1 and Stage 2 mechanism).

@@ -5,6 +5,9 @@ Parity tolerances:
 * indexing, layout, pack/unpack, reduce: bit-exact;
 * fp32 master / m / v: |gpu - ref| <= 1e-6 |ref| + 1e-9;
 * bf16 parameter copy: within 1 bf16 ulp (order-mapped integers, +0 == -0).
+The AdamW kernels compute the oracle's double update in the same order and
+round each state once, so their outputs are also checked bit for bit
+(assert_*_exact: the bar first, for a readable failure, then every bit).
 """
 import sys
 
@@ -114,3 +117,13 @@ def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str):
         i = int(np.flatnonzero(ne)[0])
         raise AssertionError(f"{what}: {int(ne.sum())} of {got.size} differ; first at {i}: "
                              f"gpu {got[i]!r} oracle {ref[i]!r}")
+
+
+def assert_fp32_exact(got: np.ndarray, ref: np.ndarray, what: str):
+    assert_fp32_close(got, ref, what)
+    assert_bits_equal(np.ascontiguousarray(got, np.float32), np.ascontiguousarray(ref, np.float32), f"{what} (bits)")
+
+
+def assert_bf16_exact(got: np.ndarray, ref: np.ndarray, what: str):
+    assert_bf16_within_1ulp(got, ref, what)
+    assert_bits_equal(np.ascontiguousarray(got, np.uint16), np.ascontiguousarray(ref, np.uint16), f"{what} (bits)")

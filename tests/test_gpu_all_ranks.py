@@ -18,7 +18,7 @@ import torch
 
 import oracle
 import zero_sharded_optimizer_zr_amd as zr
-from gpu_util import assert_bf16_within_1ulp, assert_bits_equal, assert_fp32_close, device, say
+from gpu_util import assert_bf16_exact, assert_bits_equal, assert_fp32_exact, device, say
 from zr_workloads import TINY_MLP, synth
 
 pytestmark = pytest.mark.gpu
@@ -97,8 +97,8 @@ def test_all_ranks_equal_the_unsharded_step(numels, n_d, threshold):
         p = np.zeros(x, np.uint16)
         oracle.adamw(mean, *init, p, step=STEP, **HP)
         for name, a, want in zip(("master", "m", "v"), got, init):
-            assert_fp32_close(a.cpu().numpy(), want, f"tensor {t} {name}")
-        assert_bf16_within_1ulp(params[t].cpu().numpy().view(np.uint16), p, f"tensor {t} param")
+            assert_fp32_exact(a.cpu().numpy(), want, f"tensor {t} {name}")
+        assert_bf16_exact(params[t].cpu().numpy().view(np.uint16), p, f"tensor {t} param")
     # the padding of the last rank(s) stays zero state, and its parameter slots hold bf16 zeros
     pad = slice(ref.psi_part, ref.psi_pad)
     for s in st:

@@ -38,5 +38,9 @@ def test_bench_line_on_the_tiny_shard():
     assert roof["bound"] == "hbm" and roof["unit"] == "GB/s" and roof["peak"] == 8000.0
     assert roof["frac"] == pytest.approx(roof["achieved"] / roof["peak"], abs=1e-3)
     assert roof["traffic"] is None          # counters were taken on the 7e9 shard only
+    pat = roof["pattern_ceiling"]           # the AdamW access pattern without arithmetic, same buffers
+    assert pat["ms_avg"] > 0 and pat["frac"] == pytest.approx(pat["GBps"] / roof["peak"], abs=1e-3)
+    assert pat["adamw_over_pattern"] == pytest.approx(pat["ms_avg"] / roof["algorithmic_bytes_per_launch"]
+                                                      * roof["achieved"] * 1e6, rel=1e-2)
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["value"] > 0 and cpu["cores"] >= 1 and cpu["sample"]

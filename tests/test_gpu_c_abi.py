@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import assert_bf16_within_1ulp, assert_bits_equal, assert_fp32_close, device, say
+from gpu_util import assert_bf16_exact, assert_bits_equal, assert_fp32_exact, device, say
 from zr_workloads import TINY_MLP, synth
 
 pytestmark = pytest.mark.gpu
@@ -68,7 +68,7 @@ def test_c_program_step_matches_the_oracle(tmp_path, numels, n_d, rank, n_contri
     assert_bits_equal(np.fromfile(os.path.join(d, "reduced.bin"), np.uint16), want_mean, "C ABI mean")
     got = np.fromfile(os.path.join(d, "state_out.bin"), np.float32).reshape(3, S)
     for name, a, want in zip(("master", "exp_avg", "exp_avg_sq"), got, st):
-        assert_fp32_close(a, want, f"C ABI {name}")
+        assert_fp32_exact(a, want, f"C ABI {name}")
     for t, x in enumerate(numels):
         if ref.persistent[t]:
             continue
@@ -77,5 +77,5 @@ def test_c_program_step_matches_the_oracle(tmp_path, numels, n_d, rank, n_contri
         inside = np.zeros(x, bool)
         if lo < hi:
             inside[lo - ref.offset[t]:hi - ref.offset[t]] = True
-            assert_bf16_within_1ulp(got_p[inside], flat[lo - b:hi - b], f"C ABI param tensor {t}")
+            assert_bf16_exact(got_p[inside], flat[lo - b:hi - b], f"C ABI param tensor {t}")
         assert not got_p[~inside].any(), f"C ABI unpack wrote tensor {t} outside the rank's range"

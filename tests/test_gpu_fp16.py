@@ -8,7 +8,7 @@ import torch
 
 import oracle
 import zero_sharded_optimizer_zr_amd as zr
-from gpu_util import Placed, assert_bits_equal, assert_fp32_close, device, say
+from gpu_util import Placed, assert_bits_equal, assert_fp32_exact, device, say
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,8 @@ def assert_f16_within_1ulp(got, ref, what):
         return np.where(h & 0x8000, -(h & 0x7FFF), h)
     d = np.abs(key(got) - key(ref))
     assert (d <= 1).all(), f"{what}: {int((d > 1).sum())} beyond 1 fp16 ulp"
+    # the copy is rounded from a master that equals the oracle's bit for bit
+    assert_bits_equal(np.ascontiguousarray(got, np.uint16), np.ascontiguousarray(ref, np.uint16), f"{what} (bits)")
 
 
 def assert_f16_equal(got, ref, what):
@@ -139,7 +141,7 @@ def test_adamw_f16_matches_oracle(scale, step, offs):
     torch.cuda.synchronize()
     for name, p, want in zip(("master", "m", "v"), ps, ref):
         assert p.guards_intact()
-        assert_fp32_close(p.host(), want, f"adamw f16 {name} scale {scale}")
+        assert_fp32_exact(p.host(), want, f"adamw f16 {name} scale {scale}")
     assert_f16_within_1ulp(pp.host(), rp, "adamw f16 param")
 
 
@@ -217,7 +219,7 @@ def test_fp16_steps_with_planted_overflow_match_oracle():
         o_grad = oracle.step_f16(contribs, *ref, rparam, scaler, step=t, **HP)
         assert_f16_equal(grad.cpu().numpy().view(np.uint16), o_grad, f"step {t} mean")
         for name, g, want in zip(("master", "m", "v"), gpu, ref):
-            assert_fp32_close(g.cpu().numpy(), want, f"step {t} {name}")
+            assert_fp32_exact(g.cpu().numpy(), want, f"step {t} {name}")
         assert_f16_within_1ulp(param.cpu().numpy().view(np.uint16), rparam, f"step {t} param")
         scale, good, flag, skipped = read_record(ls)
         assert (scale, good, skipped) == (scaler.scale, scaler.good_steps, scaler.skipped)

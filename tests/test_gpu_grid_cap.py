@@ -80,7 +80,7 @@ def test_reduce(monkeypatch, n_contrib, off):
     both_ways(monkeypatch, run)
 
 
-@pytest.mark.parametrize("n_contrib", [4, 9])
+@pytest.mark.parametrize("n_contrib", [4, 9, 33])
 def test_fused(monkeypatch, n_contrib):
     device()
     n = 600_007

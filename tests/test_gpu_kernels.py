@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import zero_sharded_optimizer_zr_amd as zr
-from gpu_util import (Placed, assert_bf16_within_1ulp, assert_bits_equal, assert_fp32_close, device, f32, say,
+from gpu_util import (Placed, assert_bf16_exact, assert_bits_equal, assert_fp32_exact, device, f32, say,
                       u16)
 from zr_workloads import TINY_MLP, synth
 
@@ -54,9 +54,9 @@ def _adamw_ref(g, master, m, v, step, with_param=True, hp=HP, grad_scale=1.0):
 
 def _check_adamw(got, ref, what):
     for name, a, b in zip(("master", "exp_avg", "exp_avg_sq"), got[:3], ref[:3]):
-        assert_fp32_close(a, b, f"{what} {name}")
+        assert_fp32_exact(a, b, f"{what} {name}")
     if ref[3] is not None:
-        assert_bf16_within_1ulp(got[3], ref[3], f"{what} param")
+        assert_bf16_exact(got[3], ref[3], f"{what} param")
 
 
 # ------------------------------------------------------------------ AdamW ----
@@ -68,6 +68,37 @@ def test_adamw_sizes(n):
     g, master, m, v = _adamw_inputs(n, 100 + n)
     got = _adamw_gpu(g, master, m, v, step=10)
     _check_adamw(got, _adamw_ref(g, master, m, v, 10), f"adamw n={n}")
+
+
+def _cancellation_inputs(n, seed):
+    """Step-1 inputs whose update nearly cancels the decayed master: theta *
+    (1 - lr wd) equals lr * g / (|g| + eps) up to ~1e-12, so the new master is
+    within a few 1e-10 of zero.  An fp32 evaluation of the update is off by
+    many bf16 ulps there; the kernels' double evaluation is exact."""
+    rng = np.random.default_rng(seed)
+    g = oracle.bf16_from_f32(rng.choice([-1.0, 1.0], n).astype(np.float32) * np.float32(1e-3))
+    gf = oracle.f32_from_bf16(g).astype(np.float64)
+    target = HP["lr"] * gf / (np.abs(gf) + HP["eps"]) / (1.0 - HP["lr"] * HP["weight_decay"])
+    master = (target + rng.normal(0, 1e-12, n)).astype(np.float32)
+    return g, master, np.zeros(n, np.float32), np.zeros(n, np.float32)
+
+
+def test_adamw_near_total_cancellation():
+    device()
+    g, master, m, v = _cancellation_inputs(65_536 + 5, 9)
+    ref = _adamw_ref(g, master, m, v, 1)
+    assert np.median(np.abs(ref[0])) < 1e-9
+    for offsets in ((0, 0, 0, 0, 0), (1, 0, 0, 0, 1)):     # vector body; element-wise fallback
+        _check_adamw(_adamw_gpu(g, master, m, v, step=1, offsets=offsets), ref, f"cancellation {offsets}")
+    # the fused call, one contribution equal to g (its mean is g itself), and 33
+    # (the two-pass schedule)
+    for n in (1, 4, 33):
+        pc = [Placed(g, 0) for _ in range(n)]
+        pt, pm, pv = Placed(master, 0), Placed(m, 0), Placed(v, 0)
+        pp = Placed(np.zeros(g.size, np.uint16), 0)
+        zr.zr_reduce_adamw_step([p.view for p in pc], pt.view, pm.view, pv.view, pp.view, step=1, **HP)
+        torch.cuda.synchronize()
+        _check_adamw((pt.host(), pm.host(), pv.host(), pp.host()), ref, f"fused cancellation n={n}")
 
 
 # (grad, master, m, v, param) element offsets: aligned; consistent head peel;
@@ -341,7 +372,7 @@ def _fused_vs_separate(n, size, offsets, seed, with_param=True, with_grad=True, 
     _check_adamw((ft.host(), fm.host(), fv.host(), fp.host() if fp else None), ref, f"fused vs oracle n={n}")
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 9, 64, 65])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 9, 24, 25, 64, 65])
 def test_fused_matches_separate_calls(n):
     device()
     say("fused n =", n)
@@ -366,3 +397,20 @@ def test_fused_optional_outputs_and_in_place():
     _fused_vs_separate(8, 10_001, (0, 0), 13, with_param=False, with_grad=True)
     _fused_vs_separate(4, 10_001, (2, 1), 14, in_place=True)
     _fused_vs_separate(3, 10_001, (0, 0), 15, step=1000, hp=dict(HP, lr=1e-4, weight_decay=0.1))
+
+
+def test_fused_two_pass_schedule_outputs_and_paths():
+    """Above 24 contributions the call runs the mean and AdamW as two passes,
+    with the mean in grad_out, or in param_out when only the copy is asked for
+    (AdamW then overwrites it in place), and the one-pass kernel when neither
+    output is given: every combination, both sides of the threshold, aligned,
+    head-peeled and element-wise placements, equal the separate calls bit for bit."""
+    device()
+    for n in (24, 25, 33):
+        _fused_vs_separate(n, 10_001, (0, 0), 20 + n, with_param=True, with_grad=False)
+        _fused_vs_separate(n, 10_001, (0, 0), 21 + n, with_param=False, with_grad=True)
+        _fused_vs_separate(n, 10_001, (0, 0), 22 + n, with_param=False, with_grad=False)
+        _fused_vs_separate(n, 10_001, (2, 1), 23 + n, in_place=True)
+        _fused_vs_separate(n, 4099, (3, 3), 24 + n, with_param=True, with_grad=False)
+        _fused_vs_separate(n, 4099, (1, 0), 25 + n, with_param=True, with_grad=False)
+    _fused_vs_separate(256, 3001, (0, 0), 26, with_param=True, with_grad=False)

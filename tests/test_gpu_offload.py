@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import zero_sharded_optimizer_zr_amd as zr
-from gpu_util import assert_bf16_within_1ulp, assert_fp32_close, device, say
+from gpu_util import assert_bf16_exact, assert_fp32_exact, device, say
 from zr_workloads import FLAT_7B, synth
 
 pytestmark = pytest.mark.gpu
@@ -66,8 +66,8 @@ def test_offload_matches_oracle(step, kw):
     rp = np.zeros(n, np.uint16)
     oracle.adamw(g, *ref, rp, step=step, **{**HP, **kw})
     for name, a, b in zip(("master", "m", "v"), hs, ref):
-        assert_fp32_close(a.numpy(), b, f"offload {name}")
-    assert_bf16_within_1ulp(bits(op), rp, "offload param")
+        assert_fp32_exact(a.numpy(), b, f"offload {name}")
+    assert_bf16_exact(bits(op), rp, "offload param")
 
 
 def test_offload_without_param_copy():

@@ -1,6 +1,6 @@
 """CPU tests of the host AdamW used by the ZeRO-Offload step (zr_host_adamw_step):
-parity with the oracle at the AdamW bar, bit-identity across its AVX-512 /
-AVX2 / scalar variants and with the GPU kernel's fp32 operation sequence,
+bit-identity with the oracle (the same double computation), across its
+AVX-512 / AVX2 / scalar variants,
 ragged sizes and misaligned buffers, thread counts, concurrent callers, and
 the validation of both offload entry points (no GPU is touched)."""
 import ctypes
@@ -50,73 +50,61 @@ def host_step(g, th, m, v, offset=0, threads=0, with_param=True, **kw):
     return (*[o[1].numpy().copy() for o in outs], pt.numpy().view(np.uint16).copy())
 
 
-def assert_close(got, ref, what):
-    g, r = got.astype(np.float64), ref.astype(np.float64)
-    bad = ~(np.abs(g - r) <= 1e-6 * np.abs(r) + 1e-9)
-    assert not bad.any(), f"{what}: {int(bad.sum())} outside the bar"
-
-
-def bf16_1ulp(got, ref, what):
-    o = lambda h: np.where(h.astype(np.int64) & 0x8000, -(h.astype(np.int64) & 0x7FFF), h.astype(np.int64))
-    assert (np.abs(o(got) - o(ref)) <= 1).all(), what
+def assert_bits(got, ref, what):
+    g = got.view(np.uint32) if got.dtype == np.float32 else got
+    r = ref.view(np.uint32) if ref.dtype == np.float32 else ref
+    bad = g != r
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {got.size} differ from the oracle"
 
 
 @pytest.mark.parametrize("n", [0, 1, 7, 15, 16, 17, 31, 100_003])
 @pytest.mark.parametrize("offset", [0, 1, 5])
 def test_host_adamw_matches_oracle(n, offset):
+    """The host AdamW computes the update in double, in the oracle's order of
+    operations, and rounds each state once: every bit equals the oracle's."""
     g, th, m, v = state(n, n + offset)
     ref = [th.copy(), m.copy(), v.copy()]
     rp = np.zeros(n, np.uint16)
     if n:
         oracle.adamw(g, *ref, rp, step=10, **HP)
     got = host_step(g, th, m, v, offset=offset, step=10)
-    for name, a, b in zip(("master", "m", "v"), got, ref):
-        assert_close(a, b, f"{name} n={n}")
-    bf16_1ulp(got[3], rp, "param")
+    for name, a, b in zip(("master", "m", "v", "param"), got, ref + [rp]):
+        assert_bits(a, b, f"{name} n={n}")
 
 
-@pytest.mark.parametrize("step,kw", [(1, {}), (1000, dict(lr=1e-4, weight_decay=0.1)), (3, dict(grad_scale=0.25)),
-                                     (7, dict(beta1=0.0, beta2=0.0))])
+@pytest.mark.parametrize("step,kw", [(1, {}), (10, {}), (1000, dict(lr=1e-4, weight_decay=0.1)),
+                                     (3, dict(grad_scale=0.25)), (7, dict(beta1=0.0, beta2=0.0))])
 def test_host_adamw_hyperparameters(step, kw):
     n = 70_001
     g, th, m, v = state(n, step)
     ref = [th.copy(), m.copy(), v.copy()]
     rp = np.zeros(n, np.uint16)
     oracle.adamw(g, *ref, rp, step=step, **{**HP, **kw})
-    got = host_step(g, th, m, v, step=step, **kw)
-    for name, a, b in zip(("master", "m", "v"), got, ref):
-        assert_close(a, b, f"{name} step {step}")
-    bf16_1ulp(got[3], rp, "param")
+    got = host_step(g, th, m, v, offset=3, step=step, **kw)
+    for name, a, b in zip(("master", "m", "v", "param"), got, ref + [rp]):
+        assert_bits(a, b, f"{name} step {step}")
 
 
-def gpu_op_sequence(g, th, m, v, step, lr, beta1, beta2, eps, weight_decay, grad_scale=1.0):
-    """The GPU kernel's fp32 operations, one IEEE operation at a time, on fp32
-    scalars computed in double and rounded once (numpy float32 arithmetic)."""
-    f = np.float32
-    b1, b2 = f(beta1), f(beta2)
-    c1, c2 = f(1.0 - beta1), f(1.0 - beta2)
-    dec = f(1.0 - lr * weight_decay)
-    ss = f(lr / (1.0 - beta1 ** step))
-    ib2 = f(1.0 / np.sqrt(1.0 - beta2 ** step))
-    e, gs = f(eps), f(grad_scale)
-    gr = oracle.f32_from_bf16(g) * gs
-    t = th * dec
-    mm = b1 * m + c1 * gr
-    vv = b2 * v + (c2 * gr) * gr
-    den = np.sqrt(vv) * ib2 + e
-    t = t - ss * (mm / den)
-    return t, mm, vv, oracle.bf16_from_f32(t)
-
-
-@pytest.mark.parametrize("step", [1, 10, 1000])
-def test_host_adamw_is_the_gpu_op_sequence_bit_for_bit(step):
-    n = 50_021
-    g, th, m, v = state(n, 100 + step)
-    want = gpu_op_sequence(g, th, m, v, step, **HP)
-    got = host_step(g, th, m, v, offset=3, step=step)
-    for name, a, b in zip(("master", "m", "v", "param"), got, want):
-        assert np.array_equal(a.view(np.uint32) if a.dtype == np.float32 else a,
-                              b.view(np.uint32) if b.dtype == np.float32 else b), name
+def test_host_adamw_near_total_cancellation():
+    """Elements whose update nearly cancels the decayed master (theta' within a
+    few 1e-10 of zero at step 1, where the step is lr * g / (|g| + eps)): the
+    double computation keeps them exact, so the bf16 copy equals the oracle's
+    too (an fp32 evaluation can miss it by several bf16 ulps there)."""
+    n = 4096
+    rng = np.random.default_rng(5)
+    g = oracle.bf16_from_f32(rng.choice([-1.0, 1.0], n).astype(np.float32) * np.float32(1e-3))
+    gf = oracle.f32_from_bf16(g).astype(np.float64)
+    # theta * (1 - lr wd) equals lr * g / (|g| + eps) up to a tiny offset
+    target = 5e-5 * gf / (np.abs(gf) + 1e-8) / (1.0 - 5e-5 * 0.01)
+    th = (target + rng.normal(0, 1e-12, n)).astype(np.float32)
+    m, v = np.zeros(n, np.float32), np.zeros(n, np.float32)
+    ref = [th.copy(), m.copy(), v.copy()]
+    rp = np.zeros(n, np.uint16)
+    oracle.adamw(g, *ref, rp, step=1, **HP)
+    assert np.median(np.abs(ref[0])) < 1e-9     # the cancellation is there
+    got = host_step(g, th, m, v, step=1)
+    for name, a, b in zip(("master", "m", "v", "param"), got, ref + [rp]):
+        assert_bits(a, b, f"{name} near cancellation")
 
 
 SIMD_SCRIPT = r"""

@@ -75,5 +75,25 @@ def build(verbose: bool = False, extra=(), output: str = LIBRARY) -> str:
     return output
 
 
+MEASURE_SOURCE = os.path.join(HERE, "measure", "stream_pattern.hip")
+MEASURE_LIBRARY = os.path.join(HERE, "libzr_measure.so")
+
+
+def build_measure(verbose: bool = False) -> str:
+    """The bench's measurement kernel (the AdamW kernel's access pattern
+    without its arithmetic), a library of its own beside libzr.so."""
+    cmd = ["hipcc", *FLAGS, "-shared", f"-I{CSRC}", MEASURE_SOURCE, "-o", MEASURE_LIBRARY + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if verbose and r.stderr:
+        print(r.stderr, end="", file=sys.stderr)
+    if r.returncode != 0:
+        print(r.stdout + r.stderr, file=sys.stderr)
+        raise subprocess.CalledProcessError(r.returncode, cmd)
+    os.replace(MEASURE_LIBRARY + ".tmp", MEASURE_LIBRARY)
+    return MEASURE_LIBRARY
+
+
 if __name__ == "__main__":
     print(build(verbose=True, extra=sys.argv[1:]))

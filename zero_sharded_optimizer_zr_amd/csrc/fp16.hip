@@ -196,10 +196,10 @@ __global__ __launch_bounds__(kBlock) void check_finite_kernel(const uint16_t *gr
 // ------------------------------------------------------------------ AdamW ----
 
 __device__ __forceinline__ void adamw_one_f16(const uint16_t *grad, float *master, float *m, float *v, uint16_t *param,
-                                              int64_t j, float unscale, const AdamWScalars &s)
+                                              int64_t j, double unscale, const AdamWScalars &s)
 {
     float th = master[j], mm = m[j], vv = v[j];
-    adamw_element(f16_to_f32(grad[j]) * unscale, th, mm, vv, s);
+    adamw_update((double)f16_to_f32(grad[j]) * unscale * s.grad_scale, th, mm, vv, s);
     master[j] = th;
     m[j] = mm;
     v[j] = vv;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void adamw_f16_vec_kernel(const uint16_t *g
 {
     if (ls->found_inf)  // uniform: the whole step is skipped
         return;
-    const float unscale = 1.0f / ls->scale;
+    const double unscale = 1.0 / (double)ls->scale;
     const u32x2 *g2 = reinterpret_cast<const u32x2 *>(grad + head);
     f32x4 *th4 = reinterpret_cast<f32x4 *>(master + head);
     f32x4 *m4 = reinterpret_cast<f32x4 *>(m + head);
@@ -227,13 +227,13 @@ __global__ __launch_bounds__(kBlock) void adamw_f16_vec_kernel(const uint16_t *g
         f32x4 a = load_stream(th4 + i);
         f32x4 mm = load_stream(m4 + i);
         f32x4 vv = load_stream(v4 + i);
-        float gr[4] = {f16_lo(g.x) * unscale, f16_hi(g.x) * unscale, f16_lo(g.y) * unscale, f16_hi(g.y) * unscale};
+        float gr[4] = {f16_lo(g.x), f16_hi(g.x), f16_lo(g.y), f16_hi(g.y)};
         float th[4] = {a.x, a.y, a.z, a.w};
         float mo[4] = {mm.x, mm.y, mm.z, mm.w};
         float vo[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            adamw_element(gr[e], th[e], mo[e], vo[e], s);
+            adamw_update((double)gr[e] * unscale * s.grad_scale, th[e], mo[e], vo[e], s);
         store_stream(th4 + i, f32x4{th[0], th[1], th[2], th[3]});
         store_stream(m4 + i, f32x4{mo[0], mo[1], mo[2], mo[3]});
         store_stream(v4 + i, f32x4{vo[0], vo[1], vo[2], vo[3]});
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(kBlock) void adamw_f16_scalar_kernel(const uint16_t
 {
     if (ls->found_inf)
         return;
-    const float unscale = 1.0f / ls->scale;
+    const double unscale = 1.0 / (double)ls->scale;
     for (int64_t j = global_tid(); j < numel; j += grid_stride())
         adamw_one_f16(grad, master, m, v, param, j, unscale, s);
 }

@@ -19,6 +19,11 @@
 // 5.87-5.89 TB/s for the XCD order; n = 64 5.80 against 5.49-5.54 for wider
 // batches, 5.25-5.66 for eight elements per lane).
 //
+// Above 24 contributions the entry point runs the reduce kernel and then the
+// AdamW kernel instead (see kFusedMaxN), with the mean in grad_out or, when only
+// the copy is asked for, in param_out; the bits are the same either way.  With
+// neither output the one-pass kernel runs at any n.
+//
 // Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
 // blog (111qqz.com), "ZeRO-2: why gradients can be sharded too" (after the
 // ReduceScatter each rank updates its parameter shard with its gradient shard)
@@ -31,6 +36,16 @@
 namespace zr {
 
 constexpr int kFusedBatch = 4;  // contribution loads in flight per lane
+
+// Largest contribution count the one-pass kernel takes when a two-pass schedule
+// is possible.  Its saving is the bf16 mean's write and read (2 or 4 of 2n + 26
+// bytes per element), a share that shrinks as n grows, while its n + 4
+// concurrent streams, read with 8-byte loads, lose DRAM efficiency against the
+// reduce kernel's 16-byte loads at 2 workgroups per CU.  Measured on MI355X
+// (1.05e8 elements, same buffers, one pass against reduce then AdamW): one pass
+// faster by 8% at n = 4, 7% at n = 8, 1% at n = 24; two passes faster by 0.5%
+// at n = 32 and 5.5% at n = 64.
+constexpr int32_t kFusedMaxN = 24;
 
 // Dynamic LDS reserved per workgroup (160 KB per CU): residency cap by the
 // number of concurrent streams, n contributions + 4 state/copy streams.
@@ -250,6 +265,16 @@ extern "C" zr_status zr_reduce_adamw_step(const void *const *contribs, int32_t n
     auto p = static_cast<uint16_t *>(param_out);
     auto go = static_cast<uint16_t *>(grad_out);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // Beyond kFusedMaxN contributions the mean and the update run as two passes
+    // when there is a bf16 buffer to hold the mean: grad_out, else param_out,
+    // which the AdamW pass then overwrites element by element in place.
+    uint16_t *mean_buf = go ? go : p;
+    if (n > kFusedMaxN && mean_buf) {
+        zr_status r = reduce_run(contribs, n, numel, mean_buf, st);
+        if (r != ZR_OK)
+            return r;
+        return adamw_run(mean_buf, master, exp_avg, exp_avg_sq, p, numel, s, st);
+    }
     if (n <= 8)
         return fused_launch<8>(contribs, n, master, exp_avg, exp_avg_sq, p, go, numel, d, s, st);
     if (n <= 64)

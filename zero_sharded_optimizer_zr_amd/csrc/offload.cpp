@@ -3,12 +3,13 @@
 // the bf16 gradient shard comes down over PCIe and the bf16 parameter copy goes
 // back up.
 //
-// Host AdamW: the same IEEE fp32 operations, in the same order and without
-// FMA contraction, as the GPU kernel (zr_adamw_step), on the same fp32 scalars
-// (computed in double, rounded once), so both give the same bits.  AVX-512
-// (16 lanes) or AVX2 (8 lanes) chosen at run time, scalar tails; the bf16 copy
-// is rounded to nearest even with integer arithmetic, NaN kept quiet.  Work is
-// split over a persistent pool of host threads in contiguous ranges.
+// Host AdamW: the same IEEE double operations, in the same order and without
+// FMA contraction, as the GPU kernel (zr_adamw_step), on the same double
+// scalars, each state rounded once to fp32, so both give the same bits.
+// AVX-512 (8 double lanes) or AVX2 (4 double lanes) chosen at run time,
+// scalar tails; the bf16 copy is rounded to nearest even with integer
+// arithmetic, NaN kept quiet.  Work is split over a persistent pool of host
+// threads in contiguous ranges.
 //
 // Offload pipeline: the shard is processed in chunks that fit a third of the
 // caller's pinned staging buffer (a bf16 gradient slot and a bf16 parameter
@@ -70,89 +71,106 @@ inline uint16_t host_f32_to_bf16(float f)
 void adamw_scalar(const uint16_t *g, float *th, float *m, float *v, uint16_t *p, int64_t n, const AdamWScalars &s)
 {
     for (int64_t i = 0; i < n; ++i) {
-        const float gr = host_bf16_to_f32(g[i]) * s.grad_scale;
-        float t = th[i] * s.decay;
-        const float mm = s.beta1 * m[i] + s.one_minus_beta1 * gr;
-        const float vv = s.beta2 * v[i] + (s.one_minus_beta2 * gr) * gr;
-        const float den = std::sqrt(vv) * s.inv_sqrt_bias2 + s.eps;
-        t = t - s.step_size * (mm / den);
-        th[i] = t;
-        m[i] = mm;
-        v[i] = vv;
+        const double gr = (double)host_bf16_to_f32(g[i]) * s.grad_scale;
+        double t = (double)th[i] * s.decay;
+        const double mm = s.beta1 * (double)m[i] + s.one_minus_beta1 * gr;
+        const double vv = s.beta2 * (double)v[i] + s.one_minus_beta2 * gr * gr;
+        const double m_hat = mm / s.bias1;
+        const double v_hat = vv / s.bias2;
+        t = t - s.lr * m_hat / (std::sqrt(v_hat) + s.eps);
+        th[i] = (float)t;
+        m[i] = (float)mm;
+        v[i] = (float)vv;
         if (p)
-            p[i] = host_f32_to_bf16(t);
+            p[i] = host_f32_to_bf16(th[i]);
     }
 }
 
-__attribute__((target("avx512f,avx512bw,avx512vl"))) void adamw_avx512(const uint16_t *g, float *th, float *m, float *v,
-                                                                      uint16_t *p, int64_t n, const AdamWScalars &s)
+// bf16 bits (round to nearest even, NaN kept quiet) of 8 fp32 lanes, as uint16
+__attribute__((target("avx2"))) inline __m128i bf16x8_avx2(__m256 x)
 {
-    const __m512 gs = _mm512_set1_ps(s.grad_scale), dec = _mm512_set1_ps(s.decay);
-    const __m512 b1 = _mm512_set1_ps(s.beta1), c1 = _mm512_set1_ps(s.one_minus_beta1);
-    const __m512 b2 = _mm512_set1_ps(s.beta2), c2 = _mm512_set1_ps(s.one_minus_beta2);
-    const __m512 ib2 = _mm512_set1_ps(s.inv_sqrt_bias2), eps = _mm512_set1_ps(s.eps);
-    const __m512 ss = _mm512_set1_ps(s.step_size);
-    const __m512i one = _mm512_set1_epi32(1), half = _mm512_set1_epi32(0x7fff);
-    const __m512i absm = _mm512_set1_epi32(0x7fffffff), inf = _mm512_set1_epi32(0x7f800000);
-    const __m512i quiet = _mm512_set1_epi32(0x40);
+    const __m256i one = _mm256_set1_epi32(1), half = _mm256_set1_epi32(0x7fff);
+    const __m256i absm = _mm256_set1_epi32(0x7fffffff), inf = _mm256_set1_epi32(0x7f800000);
+    const __m256i u = _mm256_castps_si256(x);
+    const __m256i hi = _mm256_srli_epi32(u, 16);
+    __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, half), _mm256_and_si256(hi, one)), 16);
+    // |u| and inf are non-negative as int32, so the signed compare orders them
+    const __m256i nan = _mm256_cmpgt_epi32(_mm256_and_si256(u, absm), inf);
+    r = _mm256_blendv_epi8(r, _mm256_or_si256(hi, _mm256_set1_epi32(0x40)), nan);
+    // 8 x int32 (all <= 0xffff) -> 8 x uint16
+    return _mm256_castsi256_si128(_mm256_permute4x64_epi64(_mm256_packus_epi32(r, r), 0x08));
+}
+
+// 8 elements per iteration, 8 double lanes.
+__attribute__((target("avx512f,avx512bw,avx512vl,avx2"))) void adamw_avx512(const uint16_t *g, float *th, float *m,
+                                                                           float *v, uint16_t *p, int64_t n,
+                                                                           const AdamWScalars &s)
+{
+    const __m512d gs = _mm512_set1_pd(s.grad_scale), dec = _mm512_set1_pd(s.decay);
+    const __m512d b1 = _mm512_set1_pd(s.beta1), c1 = _mm512_set1_pd(s.one_minus_beta1);
+    const __m512d b2 = _mm512_set1_pd(s.beta2), c2 = _mm512_set1_pd(s.one_minus_beta2);
+    const __m512d bc1 = _mm512_set1_pd(s.bias1), bc2 = _mm512_set1_pd(s.bias2);
+    const __m512d lr = _mm512_set1_pd(s.lr), eps = _mm512_set1_pd(s.eps);
     int64_t i = 0;
-    for (; i + 16 <= n; i += 16) {
-        const __m256i gh = _mm256_loadu_si256(reinterpret_cast<const __m256i *>(g + i));
-        const __m512 gr = _mm512_mul_ps(_mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(gh), 16)), gs);
-        __m512 t = _mm512_mul_ps(_mm512_loadu_ps(th + i), dec);
-        const __m512 mm = _mm512_add_ps(_mm512_mul_ps(b1, _mm512_loadu_ps(m + i)), _mm512_mul_ps(c1, gr));
-        const __m512 vv = _mm512_add_ps(_mm512_mul_ps(b2, _mm512_loadu_ps(v + i)), _mm512_mul_ps(_mm512_mul_ps(c2, gr), gr));
-        const __m512 den = _mm512_add_ps(_mm512_mul_ps(_mm512_sqrt_ps(vv), ib2), eps);
-        t = _mm512_sub_ps(t, _mm512_mul_ps(ss, _mm512_div_ps(mm, den)));
-        _mm512_storeu_ps(th + i, t);
-        _mm512_storeu_ps(m + i, mm);
-        _mm512_storeu_ps(v + i, vv);
-        if (p) {
-            const __m512i u = _mm512_castps_si512(t);
-            const __m512i hi = _mm512_srli_epi32(u, 16);
-            __m512i r = _mm512_srli_epi32(_mm512_add_epi32(_mm512_add_epi32(u, half), _mm512_and_si512(hi, one)), 16);
-            const __mmask16 nan = _mm512_cmpgt_epu32_mask(_mm512_and_si512(u, absm), inf);
-            r = _mm512_mask_mov_epi32(r, nan, _mm512_or_si512(hi, quiet));
-            _mm256_storeu_si256(reinterpret_cast<__m256i *>(p + i), _mm512_cvtepi32_epi16(r));
-        }
+    for (; i + 8 <= n; i += 8) {
+        const __m128i gh = _mm_loadu_si128(reinterpret_cast<const __m128i *>(g + i));
+        const __m256 gf = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(gh), 16));
+        const __m512d gr = _mm512_mul_pd(_mm512_cvtps_pd(gf), gs);
+        __m512d t = _mm512_mul_pd(_mm512_cvtps_pd(_mm256_loadu_ps(th + i)), dec);
+        const __m512d mm = _mm512_add_pd(_mm512_mul_pd(b1, _mm512_cvtps_pd(_mm256_loadu_ps(m + i))),
+                                         _mm512_mul_pd(c1, gr));
+        const __m512d vv = _mm512_add_pd(_mm512_mul_pd(b2, _mm512_cvtps_pd(_mm256_loadu_ps(v + i))),
+                                         _mm512_mul_pd(_mm512_mul_pd(c2, gr), gr));
+        const __m512d m_hat = _mm512_div_pd(mm, bc1);
+        const __m512d v_hat = _mm512_div_pd(vv, bc2);
+        t = _mm512_sub_pd(t, _mm512_div_pd(_mm512_mul_pd(lr, m_hat), _mm512_add_pd(_mm512_sqrt_pd(v_hat), eps)));
+        const __m256 tf = _mm512_cvtpd_ps(t);
+        _mm256_storeu_ps(th + i, tf);
+        _mm256_storeu_ps(m + i, _mm512_cvtpd_ps(mm));
+        _mm256_storeu_ps(v + i, _mm512_cvtpd_ps(vv));
+        if (p)
+            _mm_storeu_si128(reinterpret_cast<__m128i *>(p + i), bf16x8_avx2(tf));
     }
     adamw_scalar(g + i, th + i, m + i, v + i, p ? p + i : nullptr, n - i, s);
 }
 
+// 8 elements per iteration as two halves of 4 double lanes.
 __attribute__((target("avx2"))) void adamw_avx2(const uint16_t *g, float *th, float *m, float *v, uint16_t *p,
                                                 int64_t n, const AdamWScalars &s)
 {
-    const __m256 gs = _mm256_set1_ps(s.grad_scale), dec = _mm256_set1_ps(s.decay);
-    const __m256 b1 = _mm256_set1_ps(s.beta1), c1 = _mm256_set1_ps(s.one_minus_beta1);
-    const __m256 b2 = _mm256_set1_ps(s.beta2), c2 = _mm256_set1_ps(s.one_minus_beta2);
-    const __m256 ib2 = _mm256_set1_ps(s.inv_sqrt_bias2), eps = _mm256_set1_ps(s.eps);
-    const __m256 ss = _mm256_set1_ps(s.step_size);
-    const __m256i one = _mm256_set1_epi32(1), half = _mm256_set1_epi32(0x7fff);
-    const __m256i absm = _mm256_set1_epi32(0x7fffffff), inf = _mm256_set1_epi32(0x7f800000);
-    const __m256i quiet = _mm256_set1_epi32(0x40);
+    const __m256d gs = _mm256_set1_pd(s.grad_scale), dec = _mm256_set1_pd(s.decay);
+    const __m256d b1 = _mm256_set1_pd(s.beta1), c1 = _mm256_set1_pd(s.one_minus_beta1);
+    const __m256d b2 = _mm256_set1_pd(s.beta2), c2 = _mm256_set1_pd(s.one_minus_beta2);
+    const __m256d bc1 = _mm256_set1_pd(s.bias1), bc2 = _mm256_set1_pd(s.bias2);
+    const __m256d lr = _mm256_set1_pd(s.lr), eps = _mm256_set1_pd(s.eps);
     int64_t i = 0;
     for (; i + 8 <= n; i += 8) {
         const __m128i gh = _mm_loadu_si128(reinterpret_cast<const __m128i *>(g + i));
-        const __m256 gr = _mm256_mul_ps(_mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(gh), 16)), gs);
-        __m256 t = _mm256_mul_ps(_mm256_loadu_ps(th + i), dec);
-        const __m256 mm = _mm256_add_ps(_mm256_mul_ps(b1, _mm256_loadu_ps(m + i)), _mm256_mul_ps(c1, gr));
-        const __m256 vv = _mm256_add_ps(_mm256_mul_ps(b2, _mm256_loadu_ps(v + i)), _mm256_mul_ps(_mm256_mul_ps(c2, gr), gr));
-        const __m256 den = _mm256_add_ps(_mm256_mul_ps(_mm256_sqrt_ps(vv), ib2), eps);
-        t = _mm256_sub_ps(t, _mm256_mul_ps(ss, _mm256_div_ps(mm, den)));
-        _mm256_storeu_ps(th + i, t);
-        _mm256_storeu_ps(m + i, mm);
-        _mm256_storeu_ps(v + i, vv);
-        if (p) {
-            const __m256i u = _mm256_castps_si256(t);
-            const __m256i hi = _mm256_srli_epi32(u, 16);
-            __m256i r = _mm256_srli_epi32(_mm256_add_epi32(_mm256_add_epi32(u, half), _mm256_and_si256(hi, one)), 16);
-            // |u| and inf are non-negative as int32, so the signed compare orders them
-            const __m256i nan = _mm256_cmpgt_epi32(_mm256_and_si256(u, absm), inf);
-            r = _mm256_blendv_epi8(r, _mm256_or_si256(hi, quiet), nan);
-            // 8 x int32 (all <= 0xffff) -> 8 x uint16
-            const __m256i packed = _mm256_permute4x64_epi64(_mm256_packus_epi32(r, r), 0x08);
-            _mm_storeu_si128(reinterpret_cast<__m128i *>(p + i), _mm256_castsi256_si128(packed));
+        const __m256 gf = _mm256_castsi256_ps(_mm256_slli_epi32(_mm256_cvtepu16_epi32(gh), 16));
+        const __m256 thf = _mm256_loadu_ps(th + i), mf = _mm256_loadu_ps(m + i), vf = _mm256_loadu_ps(v + i);
+        __m128 to[2], mo[2], vo[2];
+        for (int h = 0; h < 2; ++h) {
+            const __m128 gq = h ? _mm256_extractf128_ps(gf, 1) : _mm256_castps256_ps128(gf);
+            const __m128 tq = h ? _mm256_extractf128_ps(thf, 1) : _mm256_castps256_ps128(thf);
+            const __m128 mq = h ? _mm256_extractf128_ps(mf, 1) : _mm256_castps256_ps128(mf);
+            const __m128 vq = h ? _mm256_extractf128_ps(vf, 1) : _mm256_castps256_ps128(vf);
+            const __m256d gr = _mm256_mul_pd(_mm256_cvtps_pd(gq), gs);
+            __m256d t = _mm256_mul_pd(_mm256_cvtps_pd(tq), dec);
+            const __m256d mm = _mm256_add_pd(_mm256_mul_pd(b1, _mm256_cvtps_pd(mq)), _mm256_mul_pd(c1, gr));
+            const __m256d vv = _mm256_add_pd(_mm256_mul_pd(b2, _mm256_cvtps_pd(vq)), _mm256_mul_pd(_mm256_mul_pd(c2, gr), gr));
+            const __m256d m_hat = _mm256_div_pd(mm, bc1);
+            const __m256d v_hat = _mm256_div_pd(vv, bc2);
+            t = _mm256_sub_pd(t, _mm256_div_pd(_mm256_mul_pd(lr, m_hat), _mm256_add_pd(_mm256_sqrt_pd(v_hat), eps)));
+            to[h] = _mm256_cvtpd_ps(t);
+            mo[h] = _mm256_cvtpd_ps(mm);
+            vo[h] = _mm256_cvtpd_ps(vv);
         }
+        const __m256 tf = _mm256_set_m128(to[1], to[0]);
+        _mm256_storeu_ps(th + i, tf);
+        _mm256_storeu_ps(m + i, _mm256_set_m128(mo[1], mo[0]));
+        _mm256_storeu_ps(v + i, _mm256_set_m128(vo[1], vo[0]));
+        if (p)
+            _mm_storeu_si128(reinterpret_cast<__m128i *>(p + i), bf16x8_avx2(tf));
     }
     adamw_scalar(g + i, th + i, m + i, v + i, p ? p + i : nullptr, n - i, s);
 }

@@ -145,6 +145,16 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
                   out, numel, d);
 }
 
+zr_status reduce_run(const void *const *contribs, int32_t n, int64_t numel, uint16_t *out, hipStream_t st)
+{
+    const MeanDivisor d = mean_divisor(n);
+    if (n <= 8)
+        return reduce_launch<8>(contribs, n, numel, out, st, d);
+    if (n <= 64)
+        return reduce_launch<64>(contribs, n, numel, out, st, d);
+    return reduce_launch<kMaxContribs>(contribs, n, numel, out, st, d);
+}
+
 }  // namespace zr
 
 using namespace zr;
@@ -174,12 +184,5 @@ extern "C" zr_status zr_reduce_slice(const void *const *contribs, int32_t n, int
     if (numel == 0)
         return ZR_OK;
 
-    const MeanDivisor d = mean_divisor(n);
-    auto o = static_cast<uint16_t *>(out);
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    if (n <= 8)
-        return reduce_launch<8>(contribs, n, numel, o, st, d);
-    if (n <= 64)
-        return reduce_launch<64>(contribs, n, numel, o, st, d);
-    return reduce_launch<kMaxContribs>(contribs, n, numel, o, st, d);
+    return reduce_run(contribs, n, numel, static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream));
 }

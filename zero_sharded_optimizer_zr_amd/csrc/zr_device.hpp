@@ -63,27 +63,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
 }
 
-// Correctly rounded fp32 square root (IEEE round to nearest even).  The
-// hardware square root (v_sqrt_f32) is only within 1 ulp, so one exact residual
-// test against each neighbour picks the right one: with s- and s+ the floats
-// next to s, the root lies below the midpoint of s- and s exactly when
-// x - s- * s <= 0, and above the midpoint of s and s+ exactly when
-// x - s+ * s > 0 (both residuals are single FMAs; a nonzero residual is at
-// least 4 times the squared half-ulp it is compared against).  Inputs below
-// 2^-96 are scaled by 2^32 first, so the hardware never sees a denormal.
-// Checked on the CPU for every finite x >= 0 and each start value within 1 ulp.
-__device__ __forceinline__ float sqrt_rn(float x)
-{
-    const bool tiny = x < 0x1p-96f;
-    const float xs = tiny ? x * 0x1p+32f : x;
-    float s = __builtin_amdgcn_sqrtf(xs);
-    const float sp = __uint_as_float(__float_as_uint(s) - 1u);
-    const float sn = __uint_as_float(__float_as_uint(s) + 1u);
-    const float rp = __fmaf_rn(-sp, s, xs), rn = __fmaf_rn(-sn, s, xs);
-    s = rp <= 0.0f ? sp : (rn > 0.0f ? sn : s);
-    return tiny ? s * 0x1p-16f : s;
-}
-
 // Global thread index and stride over a 1-D grid, 64-bit.  Every kernel is
 // launched with kBlock threads, so the block size is a compile-time constant:
 // reading blockDim.x would cost a vector load from the dispatch packet (and a
