@@ -213,20 +213,29 @@ __global__ __launch_bounds__(kBlock) void adamw_f16_vec_kernel(const uint16_t *g
                                                                int64_t groups, AdamWScalars s,
                                                                const zr_loss_scale *ls)
 {
-    if (ls->found_inf)  // uniform: the whole step is skipped
-        return;
-    const double unscale = 1.0 / (double)ls->scale;
     const u32x2 *g2 = reinterpret_cast<const u32x2 *>(grad + head);
     f32x4 *th4 = reinterpret_cast<f32x4 *>(master + head);
     f32x4 *m4 = reinterpret_cast<f32x4 *>(m + head);
     f32x4 *v4 = reinterpret_cast<f32x4 *>(v + head);
     u32x2 *p2 = kParam ? reinterpret_cast<u32x2 *>(param + head) : nullptr;
+    // The record is read once, and first used after the data loads are issued,
+    // so its latency hides behind theirs instead of delaying them; the empty
+    // asm takes the loaded data and the record together, which keeps the loads
+    // ahead of the (uniform) early return.
+    int32_t skip = ls->found_inf;
+    float scale = ls->scale;
 
     for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
         u32x2 g = load_stream(g2 + i);
         f32x4 a = load_stream(th4 + i);
         f32x4 mm = load_stream(m4 + i);
         f32x4 vv = load_stream(v4 + i);
+        int32_t sk = skip;
+        float sc = scale;
+        asm volatile("" : "+v"(g), "+v"(a), "+v"(mm), "+v"(vv), "+s"(sk), "+s"(sc));
+        if (sk)  // the whole step is skipped: nothing is written
+            return;
+        const double unscale = 1.0 / (double)sc;
         float gr[4] = {f16_lo(g.x), f16_hi(g.x), f16_lo(g.y), f16_hi(g.y)};
         float th[4] = {a.x, a.y, a.z, a.w};
         float mo[4] = {mm.x, mm.y, mm.z, mm.w};
@@ -240,12 +249,12 @@ __global__ __launch_bounds__(kBlock) void adamw_f16_vec_kernel(const uint16_t *g
         if (kParam)
             store_stream(p2 + i, u32x2{pack_f16x2(th[0], th[1]), pack_f16x2(th[2], th[3])});
     }
-    if (blockIdx.x == 0) {
+    if (blockIdx.x == 0 && !skip) {
         int64_t tail_start = head + 4 * groups;
         int64_t edge = head + (numel - tail_start);
         if ((int64_t)threadIdx.x < edge) {
             int64_t j = (int64_t)threadIdx.x < head ? (int64_t)threadIdx.x : tail_start + (threadIdx.x - head);
-            adamw_one_f16(grad, master, m, v, kParam ? param : nullptr, j, unscale, s);
+            adamw_one_f16(grad, master, m, v, kParam ? param : nullptr, j, 1.0 / (double)scale, s);
         }
     }
 }
