@@ -342,7 +342,13 @@ ZR_API zr_status zr_check_finite_f16(const void *grad, int64_t numel, zr_loss_sc
 
 /* AdamW on the fp16 gradient divided by ls->scale (then times hp->grad_scale),
  * fp16 copy into param_out (or NULL); skipped entirely while ls->found_inf is
- * set.  Same buffer rules as zr_adamw_step.
+ * set: nothing is written (the data is read before the flag is consulted).
+ * The bias corrections use hp->step exactly as passed: the library never
+ * advances or rewinds it, and a skipped call does not change it by itself.  A
+ * caller that follows the usual rule of dynamic loss scaling (the optimizer
+ * step does not advance on a skipped step) passes the count of applied steps,
+ * calls made minus ls->skipped; passing the count of calls advances t over
+ * skips.  Same buffer rules as zr_adamw_step.
  * Errors: ZR_EINVAL, ZR_EALIGN, ZR_EHIP. */
 ZR_API zr_status zr_adamw_step_f16(const void *grad, float *master, float *exp_avg, float *exp_avg_sq,
                                    void *param_out, int64_t numel, const zr_adamw_hparams *hp,

@@ -197,6 +197,46 @@ def test_loss_scale_default_window_long_run():
 
 # ------------------------------------------------------- whole sequences ----
 
+def test_fp16_step_count_is_the_callers_after_a_skip():
+    """The bias corrections use the step the caller passes: a skipped step
+    does not move them by itself.  Clean step 1, an overflowed call 2 (skipped),
+    then the third call twice from the same state: with step = 2, the count of
+    applied steps (calls made minus the record's skipped count: the rule
+    dynamic loss scaling usually follows, the optimizer step not advancing on a
+    skip), and with step = 3, the count of calls.  Each equals the oracle's
+    update with that step, and the two differ."""
+    dev = device()
+    n, size = 4, 30_001
+    st = _state(size, 91)
+    gpu = [torch.from_numpy(x.copy()).to(dev) for x in st]
+    ref = [x.copy() for x in st]
+    grad = torch.empty(size, dtype=torch.int16, device=dev)
+    ls = record()
+    scaler = oracle.LossScale()
+    for call in (1, 2):
+        contribs = scaled_contribs(n, size, 2000 + call, scaler.scale)
+        if call == 2:
+            contribs[1][7] = 0x7C00
+        zr.zr_reduce_slice_f16([torch.from_numpy(c.view(np.int16)).to(dev) for c in contribs], grad, ls)
+        zr.zr_adamw_step_f16(grad, *gpu, None, ls, step=call, **HP)
+        zr.zr_loss_scale_update(ls)
+        oracle.step_f16(contribs, *ref, None, scaler, step=call, **HP)
+    _, _, _, skipped = read_record(ls)
+    assert skipped == 1
+    contribs = scaled_contribs(n, size, 2003, scaler.scale)
+    results = {}
+    for step in (3 - skipped, 3):
+        g2 = [x.clone() for x in gpu]
+        r2 = [x.copy() for x in ref]
+        zr.zr_reduce_slice_f16([torch.from_numpy(c.view(np.int16)).to(dev) for c in contribs], grad, ls)
+        zr.zr_adamw_step_f16(grad, *g2, None, ls, step=step, **HP)
+        oracle.step_f16(contribs, *r2, None, oracle.LossScale(scaler.scale), step=step, **HP)
+        for name, g, want in zip(("master", "m", "v"), g2, r2):
+            assert_fp32_exact(g.cpu().numpy(), want, f"third call, step {step}: {name}")
+        results[step] = g2[0].cpu().numpy()
+    assert not np.array_equal(results[2], results[3])
+
+
 def test_fp16_steps_with_planted_overflow_match_oracle():
     dev = device()
     n, size, steps = 4, 60_001, 7
