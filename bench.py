@@ -297,10 +297,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f64",
         "data": "synthetic",
         "config": {"workload": w.name, "psi": info["psi"], "n_d": w.n_d, "rank": w.rank, "shard": S,
                    "contributions": n, "adamw_step": t_step, "path": "pack+reduce+adamw+unpack",
+                   "arithmetic": "AdamW in f64 on f32 master/m/v, bf16 gradient and copy; mean in f32; "
+                                 "pack/unpack bit copies",
                    "step_algorithmic_bytes": step_bytes,
                    "step_GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "kernel": "zr_adamw_step", "achieved": round(achieved, 1),
