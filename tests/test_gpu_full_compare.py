@@ -201,3 +201,150 @@ def test_full_flat_1t_nd512(pool):
     view = torch.empty(e - b, dtype=torch.bfloat16, device=device())
     zr.zr_unpack(lay, out["param"], b, e, [(view, b)])
     assert torch.equal(view.view(torch.int16), out["param"].view(torch.int16))
+
+
+# ---------------------------------------------------------------- NEXT paths --
+
+def _chunks(n, size):
+    return [(a, min(n, a + size)) for a in range(0, n, size)]
+
+
+def test_full_fp16_flat_7b_nd4(pool):
+    """The fp16 path with dynamic loss scaling on the 7e9 / N_d = 4 shard (the
+    tutorial's fp16 config, cnhsyj.com 3.1: scale 2^16): the fp16 mean of 4
+    loss-scaled contributions and the loss-scaled AdamW with its fp16 copy, every
+    element against the oracle's reduce_f16 and adamw_f16 (mean bit-exact, state
+    and copy bit-exact after the bars)."""
+    dev = device()
+    w = FLAT_7B
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    b0, e0 = zr.zr_layout_rank_range(lay, w.rank)
+    n = e0 - b0
+    scale = 65536.0
+    contribs = [synth.normal_f32(n, 1e-3 * scale, 900 + k, dev).to(torch.float16) for k in range(4)]
+    st = synth.shard_state(w, n, device=dev)
+    state = [st["master"], st["exp_avg"], st["exp_avg_sq"]]
+    before = [x.clone() for x in state]
+    ls = zr.loss_scale_record(dev)
+    zr.zr_loss_scale_init(ls, scale)
+    grad = torch.empty(n, dtype=torch.float16, device=dev)
+    param = torch.empty(n, dtype=torch.float16, device=dev)
+    say("fp16: mean of 4 contributions and loss-scaled AdamW on", n, "elements")
+    zr.zr_reduce_slice_f16(contribs, grad, ls)
+    zr.zr_adamw_step_f16(grad, *state, param, ls, step=w.steps[0], **w.hparams)
+    torch.cuda.synchronize()
+    assert int(ls.cpu()[2]) == 0, "no overflow expected"
+    pin = Pinned()
+    names = ("master", "exp_avg", "exp_avg_sq")
+    for a, b in _chunks(n, 1 << 25):
+        hc = [pin.get(f"c{k}", u16v(c)[a:b]) for k, c in enumerate(contribs)]
+        hb = [pin.get(f"b{k}", before[k][a:b]) for k in range(3)]
+        got_grad = pin.get("grad", u16v(grad)[a:b])
+        got = [pin.get(f"s{k}", state[k][a:b]) for k in range(3)]
+        got_param = pin.get("param", u16v(param)[a:b])
+
+        def work(lo, a=a, b=b, hc=hc, hb=hb, got_grad=got_grad, got=got, got_param=got_param):
+            hi = min(b - a, lo + SUB)
+            sl = slice(lo, hi)
+            o_grad = oracle.reduce_f16([x[sl] for x in hc])
+            assert_bits_equal(got_grad[sl], o_grad, f"fp16 mean [{a + lo}, {a + hi})")
+            st_ = [x[sl].copy() for x in hb]
+            o_param = np.empty(hi - lo, np.uint16)
+            oracle.adamw_f16(o_grad, *st_, o_param, step=w.steps[0], loss_scale=scale, **w.hparams)
+            for name, g, r in zip(names, got, st_):
+                assert_fp32_exact(g[sl], r, f"fp16 {name} [{a + lo}, {a + hi})")
+            assert_bits_equal(got_param[sl], o_param, f"fp16 copy [{a + lo}, {a + hi})")
+            return hi - lo
+
+        assert sum(pool.map(work, range(0, b - a, SUB))) == b - a
+    say("fp16: all", n, "elements match the oracle")
+
+
+def _random_codes(nbytes, int4, seed, dev):
+    """Codes of the other ranks' shards: int8 in [-127, 127], or int4 nibble
+    pairs in [-7, 7] (never the pattern 8)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    if int4:
+        lo = torch.randint(-7, 8, (nbytes,), generator=g, device=dev, dtype=torch.int16) & 0xF
+        hi = torch.randint(-7, 8, (nbytes,), generator=g, device=dev, dtype=torch.int16) & 0xF
+        return (lo | (hi << 4)).to(torch.uint8)
+    return torch.randint(-127, 128, (nbytes,), generator=g, device=dev, dtype=torch.int8)
+
+
+@pytest.mark.parametrize("int4", [False, True], ids=["int8", "int4"])
+def test_full_qwz_gather_flat_7b_nd4(pool, int4):
+    """The quantized AllGather (ZeRO++ qwZ on the concept page,
+    compassingai.com) on the 7e9 model over 4 ranks, block 2048: rank 0
+    quantizes its whole 1.75e9-element bf16 shard in one call (codes and block
+    scales of every block, the short last block included, against the oracle's
+    quantize over each block-aligned chunk), and the gathered 7e9 elements (rank
+    0's codes and three ranks of random codes) are rebuilt into the tensor's
+    bf16 view in one call, every element against the oracle's gathered unpack."""
+    dev = device()
+    B = 2048
+    w = FLAT_7B
+    lay = zr.zr_layout_create(w.numels, w.n_d, w.threshold)
+    ref = oracle.Layout(w.numels, w.n_d, w.threshold)
+    S, G = ref.shard, ref.psi_pad
+    per_rank = -(-S // B)
+    bytes_per_rank = -(-S // 2) if int4 else S
+    x = synth.normal_bf16(S, 0.02, 4242, dev)
+    codes = torch.empty(w.n_d * bytes_per_rank, dtype=torch.uint8 if int4 else torch.int8, device=dev)
+    scales = torch.empty(w.n_d * per_rank, dtype=torch.float32, device=dev)
+    quant = zr.zr_quantize_int4 if int4 else zr.zr_quantize_int8
+    say("qwz", "int4" if int4 else "int8", ": quantize the", S, "element shard")
+    quant(x, codes[:bytes_per_rank], scales[:per_rank], block=B)
+    torch.cuda.synchronize()
+    # rank 0's codes and scales: every block against the oracle
+    pin = Pinned()
+    oq = oracle.quantize_int4 if int4 else oracle.quantize_int8
+    chunk = (1 << 24) // B * B
+    hx = x.view(torch.int16)
+    for a, b in _chunks(S, chunk):
+        xs = pin.get("x", hx[a:b])
+        ca, cb = (a // 2, -(-b // 2)) if int4 else (a, b)
+        got_q = pin.get("q", codes[ca:cb])
+        got_s = pin.get("s", scales[a // B: -(-b // B)])
+
+        def work(lo, a=a, b=b, xs=xs, got_q=got_q, got_s=got_s):
+            hi = min(b - a, lo + SUB)     # SUB is a multiple of B and even
+            q, s = oq(np.ascontiguousarray(xs[lo:hi]), B)
+            qs = slice(lo // 2, lo // 2 + q.size) if int4 else slice(lo, hi)
+            assert_bits_equal(np.ascontiguousarray(got_q[qs]).view(np.uint8), q.view(np.uint8),
+                              f"codes [{a + lo}, {a + hi})")
+            assert_bits_equal(np.ascontiguousarray(got_s[lo // B: lo // B + s.size]), s,
+                              f"scales [{a + lo}, {a + hi})")
+            return hi - lo
+
+        assert sum(pool.map(work, range(0, b - a, SUB))) == b - a
+    # the gathered buffer: ranks 1..3 random codes and positive scales
+    codes[bytes_per_rank:] = _random_codes(3 * bytes_per_rank, int4, 77, dev).view(codes.dtype)
+    scales[per_rank:] = synth.uniform_f32(3 * per_rank, 1e-3, 78, dev) + 1e-4
+    view = torch.empty(G, dtype=torch.bfloat16, device=dev)
+    unpack = zr.zr_unpack_int4 if int4 else zr.zr_unpack_int8
+    say("qwz: rebuild the", G, "gathered elements into the view")
+    unpack(lay, codes, scales, 0, G, [view], block=B)
+    torch.cuda.synchronize()
+    ou = oracle.unpack_int4 if int4 else oracle.unpack_int8
+    hv = view.view(torch.int16)
+    for r in range(w.n_d):
+        for a, b in _chunks(S, chunk):
+            fa, fb = r * S + a, r * S + b
+            ca, cb = ((r * bytes_per_rank + a // 2, r * bytes_per_rank + -(-b // 2)) if int4
+                      else (fa, fb))
+            got = pin.get("v", hv[fa:fb])
+            hq = pin.get("q", codes[ca:cb])
+            hs = pin.get("s", scales[r * per_rank + a // B: r * per_rank + -(-b // B)])
+
+            def work(lo, fa=fa, fb=fb, got=got, hq=hq, hs=hs):
+                hi = min(fb - fa, lo + SUB)
+                out = np.zeros(hi - lo, np.uint16)
+                qs = slice(lo // 2, -(-hi // 2)) if int4 else slice(lo, hi)
+                q = np.ascontiguousarray(hq[qs]).view(np.uint8 if int4 else np.int8)
+                ou(ref, q, np.ascontiguousarray(hs[lo // B: -(-hi // B)]), B, fa + lo, fa + hi, [(out, fa + lo)])
+                assert_bits_equal(got[lo:hi], out, f"rebuilt [{fa + lo}, {fa + hi})")
+                return hi - lo
+
+            assert sum(pool.map(work, range(0, fb - fa, SUB))) == fb - fa
+    say("qwz: all", G, "rebuilt elements match the oracle")
