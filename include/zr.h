@@ -241,13 +241,17 @@ ZR_API zr_status zr_reduce_slice(const void *const *contribs, int32_t n, int64_t
 
 /*
  * One AdamW step on a shard, in place, fused with the bf16 working copy:
- *   g  = bf16->fp32(grad[i]) * grad_scale
+ *   g  = grad[i] * grad_scale
  *   th = th * (1 - lr * weight_decay)
  *   m  = beta1 * m + (1 - beta1) * g
  *   v  = beta2 * v + (1 - beta2) * g * g
- *   th = th - (lr / (1 - beta1^t)) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ *   th = th - lr * (m / (1 - beta1^t)) / (sqrt(v / (1 - beta2^t)) + eps)
  *   param_out[i] = bf16(th)   (round to nearest even)
- * computed in fp32.  Each element uses only its own gradient and state ([BLOG]
+ * computed in double, one IEEE operation at a time in this order (correctly
+ * rounded division and square root, no fused multiply-add), on the fp32 state
+ * and the bf16 gradient widened exactly and on the hyper-parameters as given;
+ * each new state is rounded once to fp32 and the copy to bf16 from that fp32
+ * master.  Each element uses only its own gradient and state ([BLOG]
  * "ZeRO-1: why optimizer states can be sharded"), so N_d shard updates
  * concatenate to the unsharded update; states are fp32 and the copy is bf16
  * ([BLOG] ledger section); the copy is made from the updated fp32 master
