@@ -9,8 +9,9 @@ ZeRO-1/2 arrangement, where every rank ends up with all parameters).  The
 persistent tensors take the AllReduce mean and the same update on every rank.
 Unpacking the full buffer then gives per-tensor parameters that must equal, per
 tensor, the oracle's plain step: the mean of the N_d gradients, then AdamW on
-the whole tensor.  Tolerances as everywhere: fp32 state within 1e-6 relative +
-1e-9 absolute, bf16 parameters within 1 ulp, the reduced gradient bit-exact.
+the whole tensor.  Bars as everywhere: the reduced gradient bit-exact; fp32
+state within 1e-6 relative + 1e-9 absolute and bf16 parameters within 1 ulp,
+and then bit for bit (the update is the oracle's double arithmetic).
 """
 import numpy as np
 import pytest

@@ -2,9 +2,10 @@
 libzr.so and the HIP runtime, no Python or torch in the process) runs one
 rank's step -- layout, pack of the rank's own gradient, mean of the
 contributions, AdamW with the bf16 copy, unpack into tensor views -- and one
-rejected call.  Its outputs must equal the oracle: the mean bit for bit, the
-fp32 state within 1e-6 relative + 1e-9 absolute, the unpacked bf16 parameters
-within 1 ulp inside the rank's range and untouched outside it."""
+rejected call.  Its outputs must equal the oracle bit for bit: the mean, the
+fp32 state (checked first against the 1e-6 relative + 1e-9 absolute bar, then
+bits) and the unpacked bf16 parameters (1 ulp first, then bits) inside the
+rank's range, which stay untouched outside it."""
 import os
 import subprocess
 

@@ -9,7 +9,7 @@ the bf16 mean, fp32 master / m / v and the bf16 parameter copy -- is then
 copied to the host chunk by chunk and compared with the oracle run over the
 same chunk from the same inputs (the state as it was before the step), on all
 host cores.  Bars: mean bit-exact; fp32 state within 1e-6 relative + 1e-9
-absolute; bf16 copy within 1 ulp.  The GPT run checks each of its 10 steps
+absolute and bf16 copy within 1 ulp, then both bit for bit.  The GPT run checks each of its 10 steps
 from the GPU's own state before that step.  The Llama shard's unpack into
 per-tensor windows and the whole 13.5 GB flat-buffer pack are compared with
 the oracle's unpack and pack over every element too.

@@ -1,8 +1,8 @@
 """GPU tests of the ZeRO-Offload step (zr_offload_adamw_step): device bf16
 gradient -> host AdamW on host fp32 states -> device bf16 parameters, through a
 pinned staging buffer in chunks.  The results must equal the GPU AdamW kernel
-(zr_adamw_step) bit for bit -- the host performs the same fp32 operations --
-and the oracle within the AdamW bar; chunk edges, ragged tails, a missing
+(zr_adamw_step) bit for bit -- the host performs the same double operations
+in the same order -- and the oracle bit for bit; chunk edges, ragged tails, a missing
 parameter copy, stream order after the kernel that produced the gradient, and
 the full 1.75e9-element shard."""
 import numpy as np

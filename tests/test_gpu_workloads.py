@@ -4,9 +4,9 @@ Shards have the real sizes (1.75e9, 1.05e8, 1.16e8 and 1.95e9 elements); the
 oracle recomputes sampled outputs one by one (about a million random elements
 plus the first and last 8192 of every buffer) from inputs snapshotted before the
 in-place update, and the layout-dependent copies are checked window by window
-against the oracle's pack/unpack.  Tolerances: reduce, pack, unpack and all
-indexing bit-exact; fp32 master / m / v within 1e-6 relative + 1e-9 absolute;
-bf16 copy within 1 ulp.
+against the oracle's pack/unpack.  Bars: reduce, pack, unpack and all indexing
+bit-exact; fp32 master / m / v within 1e-6 relative + 1e-9 absolute and bf16
+copy within 1 ulp, then both bit for bit.
 """
 import numpy as np
 import pytest
