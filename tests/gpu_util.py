@@ -119,6 +119,23 @@ def assert_bits_equal(got: np.ndarray, ref: np.ndarray, what: str):
                              f"gpu {got[i]!r} oracle {ref[i]!r}")
 
 
+def assert_bf16_equal_nan_as_class(got: np.ndarray, ref: np.ndarray, what: str):
+    """bf16 bit patterns: every element whose oracle value is a NaN must be a
+    NaN, every other element must have the oracle's bits.  A NaN's sign and
+    payload follow the arithmetic unit that made it (an x86 host gives 0 * inf
+    a negative NaN, the GPU a positive one), so they are not compared."""
+    g = np.ascontiguousarray(got, np.uint16)
+    r = np.ascontiguousarray(ref, np.uint16)
+    if g.shape != r.shape:
+        raise AssertionError(f"{what}: shape {g.shape} vs {r.shape}")
+    rn = (r & 0x7FFF) > 0x7F80
+    gn = (g & 0x7FFF) > 0x7F80
+    if (rn & ~gn).any():
+        i = int(np.flatnonzero(rn & ~gn)[0])
+        raise AssertionError(f"{what}: {int((rn & ~gn).sum())} oracle NaNs not NaN; first at {i}: gpu {g[i]:#06x}")
+    assert_bits_equal(g[~rn], r[~rn], what + " (non-NaN values)")
+
+
 def assert_fp32_exact(got: np.ndarray, ref: np.ndarray, what: str):
     assert_fp32_close(got, ref, what)
     assert_bits_equal(np.ascontiguousarray(got, np.float32), np.ascontiguousarray(ref, np.float32), f"{what} (bits)")

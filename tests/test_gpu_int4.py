@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import zero_sharded_optimizer_zr_amd as zr
-from gpu_util import Placed, assert_bits_equal, device, say
+from gpu_util import Placed, assert_bf16_equal_nan_as_class, assert_bits_equal, device, say
 from zr_workloads import FLAT_7B
 
 pytestmark = pytest.mark.gpu
@@ -169,6 +169,34 @@ def test_unpack_int4_full_range_matches_oracle(block, numels, n_d):
     for t, (g, r) in enumerate(zip(got, ref)):
         if g is not None:
             assert_bits_equal(g, r, f"tensor {t} block {block} n_d {n_d} S {lay.shard}")
+
+
+# Scale values the unpack may be handed.  The quantizer makes finite ones >= 0,
+# but the call takes any fp32: NaN, infinities, signed zeros, subnormals, values
+# whose products overflow, negative scales.
+ANY_SCALES = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-45, -3e-42, 1e-39, 1.1754942e-38, 2.0 ** 100,
+                       3.4e38, -3.4e38, 0.0123, -7.5, 1.0, 2.0 ** -126], np.float32)
+
+
+@pytest.mark.parametrize("view_off,begin", [(0, 0), (3, 0), (0, 5), (1, 2)])
+def test_unpack_int4_any_scale_values(view_off, begin):
+    """Random code bytes and scales drawn from ANY_SCALES, unpacked with
+    tensor windows whose first 8-element chunk starts on (view offset 0,
+    range from 0: one scale per chunk) and off (the other cases: a chunk may
+    straddle two blocks) a multiple of 8 in the block grid.  Bit-exact against
+    the oracle, NaN results compared as NaN."""
+    device()
+    numels = [120_017, 50_003, 170_002]
+    block = 256
+    lay, q4, s = _gathered_case(numels, 3, block, 21)
+    rng = np.random.default_rng(22 + view_off + begin)
+    q4 = rng.integers(0, 256, q4.size).astype(np.uint8)
+    s = ANY_SCALES[rng.integers(0, ANY_SCALES.size, s.size)]
+    with np.errstate(over="ignore", invalid="ignore"):  # products that overflow, 0 * inf
+        got, ref = _unpack_int4_both(lay, q4, s, block, begin, lay.psi_pad - begin, 0, view_off)
+    for t, (g, r) in enumerate(zip(got, ref)):
+        if g is not None:
+            assert_bf16_equal_nan_as_class(g, r, f"tensor {t} view offset {view_off} range from {begin}")
 
 
 @pytest.mark.parametrize("q_off,view_off", [(0, 0), (1, 0), (2, 3), (3, 1), (4, 4)])

@@ -13,9 +13,8 @@
 // split at shard boundaries, into descriptors {codes, destination, scale of the
 // first block, phase in that block, count}, passed by value in batches; every
 // workgroup rebuilds one tile of 4096 elements of one descriptor (two chunks of
-// 8 per lane, 2048 elements apart, each one aligned 16-byte store: two chunks
-// in flight per lane beat one by 12-13% and four by 4%, and capping residency
-// only slowed it), found by a binary search over the batch's tile
+// 8 per lane, 2048 elements apart, each one aligned 16-byte store), found by a
+// binary search over the batch's tile
 // prefix sums; tiles go to the 8 XCDs in contiguous runs (a grid smaller than
 // the tile count loops, every gridDim.x-th tile).  Codes come in as
 // two aligned 8-byte words per lane, funnel-shifted (v_alignbyte) when the
@@ -28,20 +27,31 @@
 // element's code, in the high four bits when that element's position in the
 // shard is odd, and a lane's 8 codes are 32 bits at a bit offset (8 per byte
 // phase, 4 for the odd nibble) uniform per descriptor, taken from two aligned
-// 4-byte words by a 64-bit shift when the offset is not 0.  Four chunks per
-// lane there (6.02 TB/s against 5.47 for two on the 7e9 gather, where half as
-// many code bytes per lane leave the loads too narrow to cover the latency).
-// The int4 code loads are ordinary cached loads: with the non-temporal hint
-// these 4-byte-per-lane loads fetched 4.3% more than the code bytes from HBM
-// (FETCH_SIZE), and ran 1% slower; cached, the fetch equals the code and scale
-// bytes.  (The int8 code loads, 8 bytes per lane, fetch exactly their bytes
-// either way and keep the hint.)
+// 4-byte words by a 64-bit shift when the offset is not 0; two chunks per lane
+// too.  The int4 code loads are ordinary cached loads: with the non-temporal
+// hint these 4-byte-per-lane loads fetched 4.3% more than the code bytes from
+// HBM (FETCH_SIZE), and ran 1% slower; cached, the fetch equals the code and
+// scale bytes.  (The int8 code loads, 8 bytes per lane, fetch exactly their
+// bytes either way and keep the hint.)
 //
-// Measured equal or slower on MI355X, same buffers: the packed hardware bf16
-// conversion (half the vector ALU work), one scale per lane where no lane's 8
-// elements can straddle two blocks (int8 -1%), the wave's scales fetched once
-// with scalar loads (int8 +1%, int4 -10%), fewer chunks per lane with either
-// (int8 one chunk -11%, int4 two -10%), and a residency cap for int4 (-6%).
+// Eight elements are rebuilt for every 16 bytes written, so the vector
+// instructions per element decide as much as HBM does.  Two things keep them
+// few.  When every chunk of a descriptor starts on a multiple of 8 in the
+// block grid (uniform per descriptor, and the case of whole shards and of
+// views aligned like them), a chunk's 8 elements share one block: one scale
+// load and no per-element scale select.  And the bf16 rounding is the packed
+// hardware conversion, one instruction per pair, whose bits equal the integer
+// round-to-nearest-even on every fp32 pattern.  On the 7e9 gather (same
+// buffers, MI355X, four sessions) they took int4 from 0.707-0.712 of the HBM
+// peak to 0.786-0.790 and int8 from 0.774-0.778 to 0.802-0.806; with them, two
+// chunks per lane beat four for int4 (0.788 against 0.727), where with the
+// integer rounding four had been faster.
+//
+// Measured equal or slower, same buffers: the wave's scales fetched once with
+// scalar loads (int8 +1%, int4 -10%), one chunk per lane (int8 -11%), a
+// residency cap for int4 (-6%), and widening codes with v_cvt_f32_ubyte and a
+// fused multiply-add by the scale minus a bias (slower, and wrong in the sign
+// of zero products).
 //
 // Reads past a descriptor's last code stay inside the aligned 8-byte (int8) or
 // 4-byte (int4) word that holds that code.
@@ -63,7 +73,7 @@ namespace {
 
 constexpr int kPerLane = 2;                          // 8-element chunks per lane (int8 codes)
 constexpr int64_t kTileLanes = kBlock * kPerLane;  // 8-element chunks per tile
-constexpr int kPerLane4 = 4;                         // the same for int4 codes
+constexpr int kPerLane4 = 2;                         // the same for int4 codes
 constexpr int64_t kTileLanes4 = kBlock * kPerLane4;
 constexpr int kMaxDesc = 64;            // 64 * 48 B of descriptors per launch
 
@@ -99,19 +109,48 @@ __device__ __forceinline__ u32x2 funnel8(u32x2 a, u32x2 b, uint32_t r)
     return u32x2{__builtin_amdgcn_alignbyte(b.x, a.y, rr), __builtin_amdgcn_alignbyte(b.y, b.x, rr)};
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values as packed bf16 in one instruction (v_cvt_pk_bf16_f32: round to
+// nearest even, NaN kept quiet with its upper payload).  Its bits equal
+// pack_bf16x2's on every one of the 2^32 fp32 bit patterns (checked on MI355X
+// for both halves), where the integer rounding takes about fifteen vector
+// instructions per pair: with 8 elements rebuilt per 16 bytes written, that
+// made these kernels as bound by vector issue as by HBM.
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 __device__ __forceinline__ uint32_t rebuild2(uint32_t codes, int k, float s0, float s1)
 {
     const float lo = (float)(int8_t)(codes >> (8 * k)) * s0;
     const float hi = (float)(int8_t)(codes >> (8 * k + 8)) * s1;
-    return pack_bf16x2(lo, hi);
+    return pack_bf16x2_hw(lo, hi);
+}
+
+// A chunk's 8 int8 codes (x.x holds elements 0-3, x.y 4-7) times one scale.
+__device__ __forceinline__ u32x4 rebuild8_one(u32x2 x, float s)
+{
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        e[j] = (float)(int8_t)(x.x >> (8 * j)) * s;
+        e[4 + j] = (float)(int8_t)(x.y >> (8 * j)) * s;
+    }
+    return u32x4{pack_bf16x2_hw(e[0], e[1]), pack_bf16x2_hw(e[2], e[3]), pack_bf16x2_hw(e[4], e[5]),
+                 pack_bf16x2_hw(e[6], e[7])};
 }
 
 // The lane's chunks of tile t: every load first, then the arithmetic and the
 // stores.  kShift: the codes' byte phase differs from the destination's (two
 // words per chunk, funnel-shifted); kFull: every chunk of the tile is inside
-// the descriptor's aligned body, so no lane needs a guard.  Both are uniform
-// per workgroup.
-template <bool kShift, bool kFull>
+// the descriptor's aligned body, so no lane needs a guard; kOne: every chunk
+// starts on a multiple of 8 in the block grid, so its 8 elements share one
+// block and one scale (blocks are multiples of 8).  All three are uniform per
+// workgroup.
+template <bool kShift, bool kFull, bool kOne>
 __device__ __forceinline__ void rebuild_chunks(const u32x2 *s2, uint32_t shift, uint16_t *out, const float *scale,
                                                int64_t e_base, int lg, int64_t c0, int64_t body)
 {
@@ -128,8 +167,10 @@ __device__ __forceinline__ void rebuild_chunks(const u32x2 *s2, uint32_t shift, 
             const int64_t e0 = e_base + 8 * c;  // position of the chunk's first element in the block grid
             const int64_t j0 = e0 >> lg;
             sa[k] = load_global(scale + j0);
-            sb[k] = load_global(scale + ((e0 + 7) >> lg));
-            split[k] = (int32_t)(((j0 + 1) << lg) - e0);
+            if (!kOne) {
+                sb[k] = load_global(scale + ((e0 + 7) >> lg));
+                split[k] = (int32_t)(((j0 + 1) << lg) - e0);
+            }
         }
     }
 #pragma unroll
@@ -138,6 +179,10 @@ __device__ __forceinline__ void rebuild_chunks(const u32x2 *s2, uint32_t shift, 
         if (!kFull && c >= body)
             break;
         const u32x2 x = kShift ? funnel8(w[k], w2[k], shift) : w[k];
+        if (kOne) {
+            store_stream(reinterpret_cast<u32x4 *>(out) + c, rebuild8_one(x, sa[k]));
+            continue;
+        }
         float s[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -152,14 +197,25 @@ __device__ __forceinline__ uint32_t rebuild2_nibbles(uint32_t codes, int k, floa
 {
     const float lo = (float)((int32_t)(codes << (28 - 4 * k)) >> 28) * s0;
     const float hi = (float)((int32_t)(codes << (24 - 4 * k)) >> 28) * s1;
-    return pack_bf16x2(lo, hi);
+    return pack_bf16x2_hw(lo, hi);
+}
+
+// A chunk's 8 int4 codes (nibble e of x is element e) times one scale.
+__device__ __forceinline__ u32x4 rebuild4_one(uint32_t x, float s)
+{
+    float e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        e[j] = (float)((int32_t)(x << (28 - 4 * j)) >> 28) * s;
+    return u32x4{pack_bf16x2_hw(e[0], e[1]), pack_bf16x2_hw(e[2], e[3]), pack_bf16x2_hw(e[4], e[5]),
+                 pack_bf16x2_hw(e[6], e[7])};
 }
 
 // int4 codes: a chunk's 8 codes are the 32 bits that start `shift` bits into
 // the aligned word pair s1[c], s1[c + 1] (shift = 8 * byte phase + 4 * nibble
 // phase, uniform per descriptor; kShift: shift != 0, so the second word holds
 // some of them).  Otherwise as rebuild_chunks.
-template <bool kShift, bool kFull>
+template <bool kShift, bool kFull, bool kOne>
 __device__ __forceinline__ void rebuild_chunks4(const uint32_t *s1, uint32_t shift, uint16_t *out, const float *scale,
                                                 int64_t e_base, int lg, int64_t c0, int64_t body)
 {
@@ -176,8 +232,10 @@ __device__ __forceinline__ void rebuild_chunks4(const uint32_t *s1, uint32_t shi
             const int64_t e0 = e_base + 8 * c;
             const int64_t j0 = e0 >> lg;
             sa[k] = load_global(scale + j0);
-            sb[k] = load_global(scale + ((e0 + 7) >> lg));
-            split[k] = (int32_t)(((j0 + 1) << lg) - e0);
+            if (!kOne) {
+                sb[k] = load_global(scale + ((e0 + 7) >> lg));
+                split[k] = (int32_t)(((j0 + 1) << lg) - e0);
+            }
         }
     }
 #pragma unroll
@@ -186,6 +244,10 @@ __device__ __forceinline__ void rebuild_chunks4(const uint32_t *s1, uint32_t shi
         if (!kFull && c >= body)
             break;
         const uint32_t x = kShift ? (uint32_t)((((uint64_t)w2[k] << 32) | w[k]) >> shift) : w[k];
+        if (kOne) {
+            store_stream(reinterpret_cast<u32x4 *>(out) + c, rebuild4_one(x, sa[k]));
+            continue;
+        }
         float s[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e)
@@ -193,6 +255,42 @@ __device__ __forceinline__ void rebuild_chunks4(const uint32_t *s1, uint32_t shi
         const u32x4 o{rebuild2_nibbles(x, 0, s[0], s[1]), rebuild2_nibbles(x, 2, s[2], s[3]),
                       rebuild2_nibbles(x, 4, s[4], s[5]), rebuild2_nibbles(x, 6, s[6], s[7])};
         store_stream(reinterpret_cast<u32x4 *>(out) + c, o);
+    }
+}
+
+// The instantiation of the chunk rebuild for the workgroup's (shift != 0, full)
+// pair; kOne as the caller found it.
+template <bool kOne>
+__device__ __forceinline__ void chunks8(const u32x2 *s2, uint32_t shift, bool full, uint16_t *out, const float *scale,
+                                        int64_t e_base, int lg, int64_t c0, int64_t body)
+{
+    if (shift == 0) {
+        if (full)
+            rebuild_chunks<false, true, kOne>(s2, shift, out, scale, e_base, lg, c0, body);
+        else
+            rebuild_chunks<false, false, kOne>(s2, shift, out, scale, e_base, lg, c0, body);
+    } else {
+        if (full)
+            rebuild_chunks<true, true, kOne>(s2, shift, out, scale, e_base, lg, c0, body);
+        else
+            rebuild_chunks<true, false, kOne>(s2, shift, out, scale, e_base, lg, c0, body);
+    }
+}
+
+template <bool kOne>
+__device__ __forceinline__ void chunks4(const uint32_t *s1, uint32_t shift, bool full, uint16_t *out,
+                                        const float *scale, int64_t e_base, int lg, int64_t c0, int64_t body)
+{
+    if (shift == 0) {
+        if (full)
+            rebuild_chunks4<false, true, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
+        else
+            rebuild_chunks4<false, false, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
+    } else {
+        if (full)
+            rebuild_chunks4<true, true, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
+        else
+            rebuild_chunks4<true, false, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
     }
 }
 
@@ -235,17 +333,10 @@ __device__ __forceinline__ void unpack_int4_tile(const QBatch &batch, int64_t ti
     const int64_t c0 = t * kTileLanes4 + threadIdx.x;
     const int64_t e_base = phase + head;
     const bool full = (t + 1) * kTileLanes4 <= body;
-    if (shift == 0) {
-        if (full)
-            rebuild_chunks4<false, true>(s1, shift, out, scale, e_base, lg, c0, body);
-        else
-            rebuild_chunks4<false, false>(s1, shift, out, scale, e_base, lg, c0, body);
-    } else {
-        if (full)
-            rebuild_chunks4<true, true>(s1, shift, out, scale, e_base, lg, c0, body);
-        else
-            rebuild_chunks4<true, false>(s1, shift, out, scale, e_base, lg, c0, body);
-    }
+    if ((e_base & 7) == 0)
+        chunks4<true>(s1, shift, full, out, scale, e_base, lg, c0, body);
+    else
+        chunks4<false>(s1, shift, full, out, scale, e_base, lg, c0, body);
 
     if (t == 0) {
         const int64_t edge = head + (n - tail_start);  // at most 7 + 7
@@ -280,17 +371,10 @@ __device__ __forceinline__ void unpack_int8_tile(const QBatch &batch, int64_t ti
     const int64_t c0 = t * kTileLanes + threadIdx.x;
     const int64_t e_base = phase + head;
     const bool full = (t + 1) * kTileLanes <= body;
-    if (shift == 0) {
-        if (full)
-            rebuild_chunks<false, true>(s2, shift, out, scale, e_base, lg, c0, body);
-        else
-            rebuild_chunks<false, false>(s2, shift, out, scale, e_base, lg, c0, body);
-    } else {
-        if (full)
-            rebuild_chunks<true, true>(s2, shift, out, scale, e_base, lg, c0, body);
-        else
-            rebuild_chunks<true, false>(s2, shift, out, scale, e_base, lg, c0, body);
-    }
+    if ((e_base & 7) == 0)
+        chunks8<true>(s2, shift, full, out, scale, e_base, lg, c0, body);
+    else
+        chunks8<false>(s2, shift, full, out, scale, e_base, lg, c0, body);
 
     if (t == 0) {
         const int64_t edge = head + (n - tail_start);  // at most 7 + 7
