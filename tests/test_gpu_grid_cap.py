@@ -161,9 +161,18 @@ def test_int4_codec(monkeypatch, block, off):
     both_ways(monkeypatch, run)
 
 
-def test_copy_and_unpack_int8(monkeypatch):
+def _many_tensors():
+    """30 tensors, two of them persistent: 30 descriptors in one unpack launch
+    (the int4 unpack's launch-order kernel)."""
+    numels = [int(x) for x in np.random.default_rng(64).integers(100_001, 160_000, 30)]
+    numels[5], numels[11] = 7, 99_999
+    return numels
+
+
+@pytest.mark.parametrize("numels", [[300_001, 7, 250_013, 123_457, 99_999, 400_003], _many_tensors()],
+                         ids=["six_tensors", "thirty_tensors"])
+def test_copy_and_unpack_int8(monkeypatch, numels):
     dev = device()
-    numels = [300_001, 7, 250_013, 123_457, 99_999, 400_003]
     lay = zr.zr_layout_create(numels, 3, 100_000)
     info = zr.zr_layout_query(lay)
     psi_pad, S = info["psi_pad"], info["shard"]

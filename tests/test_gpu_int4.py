@@ -171,6 +171,39 @@ def test_unpack_int4_full_range_matches_oracle(block, numels, n_d):
             assert_bits_equal(g, r, f"tensor {t} block {block} n_d {n_d} S {lay.shard}")
 
 
+def _many_tensor_numels(count, seed):
+    """`count` tensors of 100,001-159,999 elements, two of them persistent."""
+    rng = np.random.default_rng(seed)
+    numels = [int(x) for x in rng.integers(100_001, 160_000, count)]
+    numels[5], numels[11] = 7, 99_999
+    return numels
+
+
+def _descriptors(lay):
+    """Tensor pieces of the whole flat buffer split at shard boundaries: the
+    descriptors the unpack launches over (batches of at most 64)."""
+    return sum(len(lay.fragments(*lay.rank_range(r))) for r in range(lay.n_d))
+
+
+@pytest.mark.parametrize("count,n_d,q_off,view_off", [(30, 3, 0, 0), (30, 3, 1, 3), (68, 2, 0, 0), (68, 2, 2, 5)])
+def test_unpack_int4_many_tensors(count, n_d, q_off, view_off):
+    """A model's tensors: more than 8 descriptors in one launch (four chunks
+    per lane in launch order), and more than 64 (64 of them, then a second
+    launch of the few left: two chunks per lane in XCD runs).  Bit-exact
+    against the oracle, also with codes and views at odd offsets."""
+    device()
+    numels = _many_tensor_numels(count, count + n_d)
+    block = 512
+    lay, q4, s = _gathered_case(numels, n_d, block, count)
+    nd = _descriptors(lay)
+    assert nd > 8 and (count < 60 or 64 < nd <= 72), nd
+    say("unpack_int4 many tensors", count, "descriptors", nd, "offsets", q_off, view_off)
+    got, ref = _unpack_int4_both(lay, q4, s, block, 0, lay.psi_pad, q_off, view_off)
+    for t, (g, r) in enumerate(zip(got, ref)):
+        if g is not None:
+            assert_bits_equal(g, r, f"tensor {t} of {count}, {nd} descriptors, offsets {q_off}/{view_off}")
+
+
 # Scale values the unpack may be handed.  The quantizer makes finite ones >= 0,
 # but the call takes any fp32: NaN, infinities, signed zeros, subnormals, values
 # whose products overflow, negative scales.
@@ -178,15 +211,17 @@ ANY_SCALES = np.array([np.nan, np.inf, -np.inf, 0.0, -0.0, 1e-45, -3e-42, 1e-39,
                        3.4e38, -3.4e38, 0.0123, -7.5, 1.0, 2.0 ** -126], np.float32)
 
 
-@pytest.mark.parametrize("view_off,begin", [(0, 0), (3, 0), (0, 5), (1, 2)])
-def test_unpack_int4_any_scale_values(view_off, begin):
+@pytest.mark.parametrize("view_off,begin,many", [(0, 0, False), (3, 0, False), (0, 5, False), (1, 2, False),
+                                                (0, 0, True), (3, 1, True)])
+def test_unpack_int4_any_scale_values(view_off, begin, many):
     """Random code bytes and scales drawn from ANY_SCALES, unpacked with
     tensor windows whose first 8-element chunk starts on (view offset 0,
     range from 0: one scale per chunk) and off (the other cases: a chunk may
-    straddle two blocks) a multiple of 8 in the block grid.  Bit-exact against
-    the oracle, NaN results compared as NaN."""
+    straddle two blocks) a multiple of 8 in the block grid, for a few tensors
+    and for a model's many.  Bit-exact against the oracle, NaN results
+    compared as NaN."""
     device()
-    numels = [120_017, 50_003, 170_002]
+    numels = _many_tensor_numels(30, 9) if many else [120_017, 50_003, 170_002]
     block = 256
     lay, q4, s = _gathered_case(numels, 3, block, 21)
     rng = np.random.default_rng(22 + view_off + begin)

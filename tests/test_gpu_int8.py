@@ -243,6 +243,26 @@ def test_unpack_int8_full_range_matches_oracle(block, n_d):
             assert_bits_equal(g, r, f"tensor {t} block {block} n_d {n_d}")
 
 
+@pytest.mark.parametrize("count,n_d,q_off,view_off", [(30, 3, 0, 0), (68, 2, 3, 5)])
+def test_unpack_int8_many_tensors(count, n_d, q_off, view_off):
+    """A model's tensors: 30 descriptors in one launch, and 67 (a launch of 64,
+    then one of 3).  Bit-exact against the oracle, also with codes and views at
+    odd offsets."""
+    device()
+    rng = np.random.default_rng(count + n_d)
+    numels = [int(x) for x in rng.integers(100_001, 160_000, count)]
+    numels[5], numels[11] = 7, 99_999
+    block = 512
+    lay, q, s = _gathered_case(numels, n_d, block, count)
+    nd = sum(len(lay.fragments(*lay.rank_range(r))) for r in range(lay.n_d))
+    assert nd > 8 and (count < 60 or 64 < nd <= 72), nd
+    say("unpack_int8 many tensors", count, "descriptors", nd)
+    got, ref = _unpack_int8_both(lay, q, s, block, 0, lay.psi_pad, q_off, view_off)
+    for t, (g, r) in enumerate(zip(got, ref)):
+        if g is not None:
+            assert_bits_equal(g, r, f"tensor {t} of {count}, {nd} descriptors, offsets {q_off}/{view_off}")
+
+
 # Scale values the unpack may be handed.  The quantizer makes finite ones >= 0,
 # but the call takes any fp32: NaN, infinities, signed zeros, subnormals, values
 # whose products overflow, negative scales.

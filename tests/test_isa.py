@@ -29,9 +29,10 @@ CSRC = os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "csrc")
 #   copy: aligned or funnel-shifted (two) loads, one store per lane.
 #   int8 quantizer: 4 chunks of 16-byte loads per tile, 8-byte code stores
 #   (int4: 4-byte code stores, beside the scale stores of the same width).
-#   int8 / int4 unpack: the 16-byte stores of the rebuilt chunks (two per lane)
-#   over the instantiations (code phase, whole tile, one scale per chunk), as
-#   compiled; a change of the count is a change of the kernel's shape.
+#   int8 / int4 unpack: the 16-byte stores of the rebuilt chunks (two per lane;
+#   int4 two or four) over the instantiations (code phase, whole tile, one scale
+#   per chunk), as compiled; a change of the count is a change of the kernel's
+#   shape.
 KERNELS = [
     ("adamw.hip", "adamw_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                             "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
@@ -45,7 +46,8 @@ KERNELS = [
     ("quant.hip", "quantize_vec_kernelILi2048ELi127E", {"global_load_dwordx4": 4, "global_store_dwordx2": 4}),
     ("quant.hip", "quantize_vec_kernelILi2048ELi7E", {"global_load_dwordx4": 4}),
     ("quant.hip", "dequantize_vec_kernelILi2048ELi7E", {"global_store_dwordx4": 4}),
-    ("unpack_quant.hip", "unpack_int4_kernel", {"global_store_dwordx4": 9}),
+    ("unpack_quant.hip", "unpack_int4_kernelILi2ELb1E", {"global_store_dwordx4": 9}),
+    ("unpack_quant.hip", "unpack_int4_kernelILi4ELb0E", {"global_store_dwordx4": 25}),
 ]
 
 

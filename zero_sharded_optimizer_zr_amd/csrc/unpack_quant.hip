@@ -14,9 +14,9 @@
 // first block, phase in that block, count}, passed by value in batches; every
 // workgroup rebuilds one tile of 4096 elements of one descriptor (two chunks of
 // 8 per lane, 2048 elements apart, each one aligned 16-byte store), found by a
-// binary search over the batch's tile
-// prefix sums; tiles go to the 8 XCDs in contiguous runs (a grid smaller than
-// the tile count loops, every gridDim.x-th tile).  Codes come in as
+// binary search over the batch's compact array of first tiles; tiles go to the
+// 8 XCDs in contiguous runs (a grid smaller than the tile count loops, every
+// gridDim.x-th tile).  Codes come in as
 // two aligned 8-byte words per lane, funnel-shifted (v_alignbyte) when the
 // source's byte phase differs from the destination's; a lane's 8 elements
 // span at most two blocks (blocks are >= 256 elements and a descriptor lies in
@@ -27,8 +27,10 @@
 // element's code, in the high four bits when that element's position in the
 // shard is odd, and a lane's 8 codes are 32 bits at a bit offset (8 per byte
 // phase, 4 for the odd nibble) uniform per descriptor, taken from two aligned
-// 4-byte words by a 64-bit shift when the offset is not 0; two chunks per lane
-// too.  The int4 code loads are ordinary cached loads: with the non-temporal
+// 4-byte words by a 64-bit shift when the offset is not 0.  Chunks per lane
+// and tile order are chosen per launch (launch_batches): two in XCD runs for a
+// batch of a few whole shards, four in launch order for a batch of a model's
+// tensors.  The int4 code loads are ordinary cached loads: with the non-temporal
 // hint these 4-byte-per-lane loads fetched 4.3% more than the code bytes from
 // HBM (FETCH_SIZE), and ran 1% slower; cached, the fetch equals the code and
 // scale bytes.  (The int8 code loads, 8 bytes per lane, fetch exactly their
@@ -43,9 +45,7 @@
 // hardware conversion, one instruction per pair, whose bits equal the integer
 // round-to-nearest-even on every fp32 pattern.  On the 7e9 gather (same
 // buffers, MI355X, four sessions) they took int4 from 0.707-0.712 of the HBM
-// peak to 0.786-0.790 and int8 from 0.774-0.778 to 0.802-0.806; with them, two
-// chunks per lane beat four for int4 (0.788 against 0.727), where with the
-// integer rounding four had been faster.
+// peak to 0.786-0.790 and int8 from 0.774-0.778 to 0.802-0.806.
 //
 // Measured equal or slower, same buffers: the wave's scales fetched once with
 // scalar loads (int8 +1%, int4 -10%), one chunk per lane (int8 -11%), a
@@ -73,16 +73,17 @@ namespace {
 
 constexpr int kPerLane = 2;                          // 8-element chunks per lane (int8 codes)
 constexpr int64_t kTileLanes = kBlock * kPerLane;  // 8-element chunks per tile
-constexpr int kPerLane4 = 2;                         // the same for int4 codes
-constexpr int64_t kTileLanes4 = kBlock * kPerLane4;
-constexpr int kMaxDesc = 64;            // 64 * 48 B of descriptors per launch
+// int4 codes: chunks per lane, per launch (see launch_batches)
+constexpr int kPerLane4Few = 2;   // a batch of a few large descriptors
+constexpr int kPerLane4Many = 4;  // a batch of many
+constexpr int kFewDesc = 8;
+constexpr int kMaxDesc = 64;            // 64 * (8 + 40) B of descriptors per launch
 
 struct QDesc {
     const int8_t *src;   // code of the first element
     uint16_t *dst;       // its place in the tensor view
     const float *scale;  // scale of the block holding the first element
     int64_t n;           // elements
-    int64_t tile_begin;  // prefix sum of tiles within the batch
     int32_t phase;       // position of the first element inside its block
     int32_t reserved;
 };
@@ -90,6 +91,7 @@ struct QDesc {
 struct QBatch {
     int32_t count;
     int32_t lg_block;
+    int64_t first_tile[kMaxDesc];  // prefix sums of the descriptors' tiles
     QDesc d[kMaxDesc];
 };
 
@@ -215,15 +217,15 @@ __device__ __forceinline__ u32x4 rebuild4_one(uint32_t x, float s)
 // the aligned word pair s1[c], s1[c + 1] (shift = 8 * byte phase + 4 * nibble
 // phase, uniform per descriptor; kShift: shift != 0, so the second word holds
 // some of them).  Otherwise as rebuild_chunks.
-template <bool kShift, bool kFull, bool kOne>
+template <int PL, bool kShift, bool kFull, bool kOne>
 __device__ __forceinline__ void rebuild_chunks4(const uint32_t *s1, uint32_t shift, uint16_t *out, const float *scale,
                                                 int64_t e_base, int lg, int64_t c0, int64_t body)
 {
-    uint32_t w[kPerLane4], w2[kPerLane4];
-    float sa[kPerLane4], sb[kPerLane4];
-    int32_t split[kPerLane4];
+    uint32_t w[PL], w2[PL];
+    float sa[PL], sb[PL];
+    int32_t split[PL];
 #pragma unroll
-    for (int k = 0; k < kPerLane4; ++k) {
+    for (int k = 0; k < PL; ++k) {
         const int64_t c = c0 + k * kBlock;
         if (kFull || c < body) {
             w[k] = load_global(s1 + c);  // cached: see the header
@@ -239,7 +241,7 @@ __device__ __forceinline__ void rebuild_chunks4(const uint32_t *s1, uint32_t shi
         }
     }
 #pragma unroll
-    for (int k = 0; k < kPerLane4; ++k) {
+    for (int k = 0; k < PL; ++k) {
         const int64_t c = c0 + k * kBlock;
         if (!kFull && c >= body)
             break;
@@ -277,49 +279,54 @@ __device__ __forceinline__ void chunks8(const u32x2 *s2, uint32_t shift, bool fu
     }
 }
 
-template <bool kOne>
+template <int PL, bool kOne>
 __device__ __forceinline__ void chunks4(const uint32_t *s1, uint32_t shift, bool full, uint16_t *out,
                                         const float *scale, int64_t e_base, int lg, int64_t c0, int64_t body)
 {
     if (shift == 0) {
         if (full)
-            rebuild_chunks4<false, true, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
+            rebuild_chunks4<PL, false, true, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
         else
-            rebuild_chunks4<false, false, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
+            rebuild_chunks4<PL, false, false, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
     } else {
         if (full)
-            rebuild_chunks4<true, true, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
+            rebuild_chunks4<PL, true, true, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
         else
-            rebuild_chunks4<true, false, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
+            rebuild_chunks4<PL, true, false, kOne>(s1, shift, out, scale, e_base, lg, c0, body);
     }
 }
 
-__device__ __forceinline__ const QDesc &find_desc(const QBatch &batch, int64_t tile)
+// Index of the descriptor holding `tile`: a binary search over the batch's
+// compact array of first tiles (uniform per workgroup, scalar loads).
+__device__ __forceinline__ int find_desc(const QBatch &batch, int64_t tile)
 {
     int lo = 0, hi = batch.count - 1;
     while (lo < hi) {
-        int mid = (lo + hi + 1) >> 1;
-        if (batch.d[mid].tile_begin <= tile)
+        const int mid = (lo + hi + 1) >> 1;
+        if (batch.first_tile[mid] <= tile)
             lo = mid;
         else
             hi = mid - 1;
     }
-    return batch.d[lo];
+    return lo;
 }
 
 // int4: D.src is the byte holding the code of the descriptor's first element,
 // in its high four bits when the element's position in the shard is odd (its
 // position in the block, D.phase, has the same parity: blocks are even).
+template <int PL>
 __device__ __forceinline__ void unpack_int4_tile(const QBatch &batch, int64_t tile)
 {
-    const QDesc &D = find_desc(batch, tile);
+    const int k = find_desc(batch, tile);
+    const QDesc &D = batch.d[k];
+    constexpr int64_t kTileLanes4 = kBlock * PL;
     const uint8_t *src = reinterpret_cast<const uint8_t *>(D.src);
     uint16_t *dst = D.dst;
     const float *scale = D.scale;
     const int64_t n = D.n;
     const int64_t phase = D.phase;
     const int lg = batch.lg_block;
-    const int64_t t = tile - D.tile_begin;
+    const int64_t t = tile - batch.first_tile[k];
 
     const int64_t head = head_of(dst, n);
     const int64_t body = (n - head) / 8;
@@ -334,9 +341,9 @@ __device__ __forceinline__ void unpack_int4_tile(const QBatch &batch, int64_t ti
     const int64_t e_base = phase + head;
     const bool full = (t + 1) * kTileLanes4 <= body;
     if ((e_base & 7) == 0)
-        chunks4<true>(s1, shift, full, out, scale, e_base, lg, c0, body);
+        chunks4<PL, true>(s1, shift, full, out, scale, e_base, lg, c0, body);
     else
-        chunks4<false>(s1, shift, full, out, scale, e_base, lg, c0, body);
+        chunks4<PL, false>(s1, shift, full, out, scale, e_base, lg, c0, body);
 
     if (t == 0) {
         const int64_t edge = head + (n - tail_start);  // at most 7 + 7
@@ -351,14 +358,15 @@ __device__ __forceinline__ void unpack_int4_tile(const QBatch &batch, int64_t ti
 
 __device__ __forceinline__ void unpack_int8_tile(const QBatch &batch, int64_t tile)
 {
-    const QDesc &D = find_desc(batch, tile);
+    const int k = find_desc(batch, tile);
+    const QDesc &D = batch.d[k];
     const int8_t *src = D.src;
     uint16_t *dst = D.dst;
     const float *scale = D.scale;
     const int64_t n = D.n;
     const int64_t phase = D.phase;
     const int lg = batch.lg_block;
-    const int64_t t = tile - D.tile_begin;
+    const int64_t t = tile - batch.first_tile[k];
 
     const int64_t head = head_of(dst, n);
     const int64_t body = (n - head) / 8;  // aligned 16-byte destination chunks
@@ -385,42 +393,54 @@ __device__ __forceinline__ void unpack_int8_tile(const QBatch &batch, int64_t ti
     }
 }
 
-// Tiles in XCD runs (the grid is a multiple of kXcds); a workgroup takes tile
-// xcd_first_tile(), then every gridDim.x-th after it.
+// int8: tiles in XCD runs (the grid is a multiple of kXcds); a workgroup takes
+// tile xcd_first_tile(), then every gridDim.x-th after it.
 __global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64_t total_tiles)
 {
     for (int64_t tile = xcd_first_tile(); tile < total_tiles; tile += gridDim.x)
         unpack_int8_tile(batch, tile);
 }
 
+// int4: PL chunks per lane; tiles in XCD runs (kXcdOrder) or in launch order.
+template <int PL, bool kXcdOrder>
 __global__ __launch_bounds__(kBlock) void unpack_int4_kernel(QBatch batch, int64_t total_tiles)
 {
-    for (int64_t tile = xcd_first_tile(); tile < total_tiles; tile += gridDim.x)
-        unpack_int4_tile(batch, tile);
+    for (int64_t tile = kXcdOrder ? xcd_first_tile() : (int64_t)blockIdx.x; tile < total_tiles; tile += gridDim.x)
+        unpack_int4_tile<PL>(batch, tile);
 }
 
+// int4 batches of at most kFewDesc descriptors (whole shards: a flat model's
+// gather) run two chunks per lane with the tiles in XCD runs; larger batches
+// (a model's tensors) run four chunks per lane in launch order.  Measured on
+// the gathers of the 7e9 flat model over 4 ranks and of the Llama- and
+// GPT-style layouts (MI355X, same buffers): 0.790 against 0.760 for the first,
+// 0.786-0.800 against 0.683-0.685 for the others.
 zr_status launch_batches(const std::vector<QDesc> &pieces, int lg_block, bool int4, hipStream_t st)
 {
     size_t i = 0;
     while (i < pieces.size()) {
         QBatch batch{};
         batch.lg_block = lg_block;
+        const int count = (int)std::min<size_t>(pieces.size() - i, (size_t)kMaxDesc);
+        const bool few = count <= kFewDesc;
+        const int64_t lanes = kBlock * (int4 ? (few ? kPerLane4Few : kPerLane4Many) : kPerLane);
         int64_t tiles = 0;
-        int count = 0;
-        while (i < pieces.size() && count < kMaxDesc) {
-            const QDesc &p = pieces[i];
+        for (int k = 0; k < count; ++k) {
+            const QDesc &p = pieces[i + k];
             const int64_t body = (p.n - head_of(p.dst, p.n)) / 8;
-            const int64_t lanes = int4 ? kTileLanes4 : kTileLanes;
-            const int64_t nt = std::max<int64_t>(1, (body + lanes - 1) / lanes);
-            batch.d[count] = p;
-            batch.d[count].tile_begin = tiles;
-            tiles += nt;
-            ++count;
-            ++i;
+            batch.d[k] = p;
+            batch.first_tile[k] = tiles;
+            tiles += std::max<int64_t>(1, (body + lanes - 1) / lanes);
         }
         batch.count = count;
-        zr_status s = int4 ? launch(unpack_int4_kernel, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles)
-                           : launch(unpack_int8_kernel, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
+        i += count;
+        zr_status s;
+        if (!int4)
+            s = launch(unpack_int8_kernel, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
+        else if (few)
+            s = launch(unpack_int4_kernel<kPerLane4Few, true>, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
+        else
+            s = launch(unpack_int4_kernel<kPerLane4Many, false>, grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
         if (s != ZR_OK)
             return s;
     }
