@@ -64,7 +64,9 @@ def test_reduce_f16_bit_exact(n):
     size = 20_000 + n
     contribs = scaled_contribs(n, size, n)
     ref = oracle.reduce_f16(contribs)
-    for offs, oo in (([0] * n, 0), ([3] * n, 3), ([k % 5 for k in range(n)], 1)):
+    # aligned; a common 16-byte phase; mixed phases; heads of 48 and 3 elements to the
+    # output's 128-byte line
+    for offs, oo in (([0] * n, 0), ([3] * n, 3), ([k % 5 for k in range(n)], 1), ([16] * n, 16), ([61] * n, 61)):
         placed = [Placed(c, o) for c, o in zip(contribs, offs)]
         out = Placed(np.zeros(size, np.uint16), oo)
         ls = record()
@@ -103,7 +105,7 @@ def test_reduce_f16_extremes_subnormals_and_flag():
 def test_check_finite(size, pos):
     device()
     g = f16(np.random.default_rng(size).normal(0, 100, size))
-    for off in (0, 3):
+    for off in (0, 3, 40, 61):
         p = Placed(g, off)
         ls = record()
         zr.zr_check_finite_f16(p.view, ls)
@@ -124,7 +126,10 @@ def _state(n, seed):
 
 
 @pytest.mark.parametrize("scale,step,offs", [(S0, 1, (0, 0)), (2.0 ** 10, 10, (0, 0)), (1.0, 3, (3, 1)),
-                                             (2.0 ** 20, 1000, (1, 1)), (S0, 2, (2, 0))])
+                                             (2.0 ** 20, 1000, (1, 1)), (S0, 2, (2, 0)),
+                                             # element offsets from a 128-byte line (heads up to 63)
+                                             (S0, 4, (8, 8)), (S0, 5, (40, 40)), (S0, 6, (61, 61)),
+                                             (S0, 7, (12, 8))])
 def test_adamw_f16_matches_oracle(scale, step, offs):
     device()
     n = 50_003

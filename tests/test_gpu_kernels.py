@@ -124,6 +124,26 @@ def test_adamw_every_path_gives_the_same_bits():
                 assert_bits_equal(a, b, f"path {off} vs aligned: {name}")
 
 
+# (grad, master, m, v, param) element offsets from a 128-byte line: every array
+# sliced at one offset (heads of 56, 24 or 20 elements that put the fp32 and the
+# bf16 arrays on lines together, and 61 that puts them on lines at 3), and bf16
+# arrays at another phase than the fp32 ones (the head follows master alone).
+LINE_OFFSETS = [(8, 8, 8, 8, 8), (12, 12, 12, 12, 12), (40, 40, 40, 40, 40), (61, 61, 61, 61, 61),
+                (12, 8, 8, 8, 12), (4, 24, 24, 24, 36)]
+
+
+@pytest.mark.parametrize("n", [1, 50, 63, 64, 65, 200, 4099, 50_011])
+def test_adamw_line_heads(n):
+    """The vector body starts where master (and, when one index does both, the
+    gradient) starts a 128-byte line: heads of up to 63 elements, done
+    element-wise with the tail, at every length from all-element-wise up."""
+    device()
+    g, master, m, v = _adamw_inputs(n, 41 + n)
+    ref = _adamw_ref(g, master, m, v, 6)
+    for off in LINE_OFFSETS:
+        _check_adamw(_adamw_gpu(g, master, m, v, step=6, offsets=off), ref, f"adamw n={n} offsets {off}")
+
+
 @pytest.mark.parametrize("step,hp,scale,m_std,v_high", [
     (1, HP, 1.0, 0.0, 0.0),
     (1000, dict(HP, lr=1e-4, weight_decay=0.1), 1.0, 1e-4, 1e-6),
@@ -211,6 +231,17 @@ def test_reduce_bit_exact(n):
     offs = [int(x) for x in rng.integers(0, 8, n)]
     assert_bits_equal(_reduce_gpu(contribs, offs, int(rng.integers(0, 8))), ref, f"reduce n={n} offsets")
     assert_bits_equal(_reduce_gpu(contribs, [3] * n, 3), ref, f"reduce n={n} common phase")
+
+
+@pytest.mark.parametrize("off", [8, 16, 40, 61, 63])
+def test_reduce_line_heads(off):
+    """Contributions and output at one element offset from a 128-byte line: the
+    vector body starts on the output's line (a head of up to 63 elements)."""
+    device()
+    for size in (1, 63, 64, 65, 130, 5003):
+        contribs = [_bits(synth.normal_bf16(size, 1e-3, 700 + 7 * off + k)) for k in range(4)]
+        ref = oracle.reduce(contribs)
+        assert_bits_equal(_reduce_gpu(contribs, [off] * 4, off), ref, f"reduce size {size} offset {off}")
 
 
 @pytest.mark.parametrize("size", [0, 1, 5, 8, 17, 2048, 2049 * 8 + 3])
@@ -370,6 +401,16 @@ def _fused_vs_separate(n, size, offsets, seed, with_param=True, with_grad=True, 
     o_grad = oracle.reduce(contribs)
     ref = _adamw_ref(o_grad, master, m, v, step, with_param=with_param, hp=hp)
     _check_adamw((ft.host(), fm.host(), fv.host(), fp.host() if fp else None), ref, f"fused vs oracle n={n}")
+
+
+@pytest.mark.parametrize("n,size", [(4, 65), (4, 5003), (8, 200), (8, 5003), (33, 5003)])
+@pytest.mark.parametrize("offsets", [(8, 8), (12, 12), (40, 40), (61, 61), (12, 8)])
+def test_fused_line_heads(n, size, offsets):
+    """(contribution, state) element offsets from a 128-byte line, as in the
+    AdamW line-head test: the fused call (one pass, and two passes above 24
+    contributions) equals the two calls and the oracle."""
+    device()
+    _fused_vs_separate(n, size, offsets, 900 + n + size)
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8, 9, 24, 25, 64, 65])

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t *grad,
 
     if (blockIdx.x == 0) {
         int64_t tail_start = head + 4 * groups;
-        int64_t edge = head + (numel - tail_start);  // at most 3 + 3
+        int64_t edge = head + (numel - tail_start);  // at most 63 + 3
         if ((int64_t)threadIdx.x < edge) {
             int64_t j = (int64_t)threadIdx.x < head ? (int64_t)threadIdx.x : tail_start + (threadIdx.x - head);
             adamw_one(grad, master, m, v, kParam ? param : nullptr, j, s);
@@ -113,9 +113,7 @@ zr_status adamw_run(const uint16_t *g, float *master, float *exp_avg, float *exp
 {
     // elements before master reaches a 16-byte boundary; the other buffers must
     // then be aligned too (16 B for fp32, 8 B for bf16) for the vector body
-    int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(master) & 15)) & 15) / 4);
-    if (head > numel)
-        head = numel;
+    const int64_t head = line_head32(master, g, numel);
     bool vec = aligned_to(exp_avg + head, 16) && aligned_to(exp_avg_sq + head, 16) && aligned_to(g + head, 8) &&
                (!p || aligned_to(p + head, 8));
     if (vec) {

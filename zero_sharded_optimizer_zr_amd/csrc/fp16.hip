@@ -280,9 +280,7 @@ static zr_status reduce_f16_launch(const void *const *contribs, int32_t n, int64
     for (int32_t k = 0; k < n; ++k)
         c.p[k] = static_cast<const uint16_t *>(contribs[k]);
     const MeanDivisor d = mean_divisor(n);
-    int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(out) & 15)) & 15) / 2);
-    if (head > numel)
-        head = numel;
+    const int64_t head = line_head16(out, numel);
     bool vec = true;
     for (int32_t k = 0; k < n && vec; ++k)
         vec = aligned_to(c.p[k] + head, 16);
@@ -405,9 +403,7 @@ extern "C" zr_status zr_check_finite_f16(const void *grad, int64_t numel, zr_los
     if (numel == 0)
         return ZR_OK;
     auto g = static_cast<const uint16_t *>(grad);
-    int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(g) & 15)) & 15) / 2);
-    if (head > numel)
-        head = numel;
+    const int64_t head = line_head16(g, numel);
     const int64_t groups = (numel - head) / 8;
     return launch(check_finite_kernel, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock), 0,
                   static_cast<hipStream_t>(stream), g, numel, head, groups, ls);
@@ -445,9 +441,7 @@ extern "C" zr_status zr_adamw_step_f16(const void *grad, float *master, float *e
     auto g = static_cast<const uint16_t *>(grad);
     auto p = static_cast<uint16_t *>(param_out);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(master) & 15)) & 15) / 4);
-    if (head > numel)
-        head = numel;
+    const int64_t head = line_head32(master, g, numel);
     bool vec = aligned_to(exp_avg + head, 16) && aligned_to(exp_avg_sq + head, 16) && aligned_to(g + head, 8) &&
                (!p || aligned_to(p + head, 8));
     if (!vec)

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(ContribTable<MaxN> c,
 
     if (blockIdx.x == 0) {
         int64_t tail_start = head + 4 * groups;
-        int64_t edge = head + (numel - tail_start);  // at most 3 + 3
+        int64_t edge = head + (numel - tail_start);  // at most 63 + 3
         if ((int64_t)threadIdx.x < edge) {
             int64_t j = (int64_t)threadIdx.x < head ? (int64_t)threadIdx.x : tail_start + (threadIdx.x - head);
             fused_one(c, n, master, m, v, kParam ? param : nullptr, kGrad ? gout : nullptr, j, d, s);
@@ -173,9 +173,7 @@ static zr_status fused_launch(const void *const *contribs, int32_t n, float *mas
     ContribTable<MaxN> c = {};
     for (int32_t k = 0; k < n; ++k)
         c.p[k] = static_cast<const uint16_t *>(contribs[k]);
-    int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(master) & 15)) & 15) / 4);
-    if (head > numel)
-        head = numel;
+    const int64_t head = line_head32(master, c.p[0], numel);
     bool vec = aligned_to(m + head, 16) && aligned_to(v + head, 16) && (!param || aligned_to(param + head, 8)) &&
                (!gout || aligned_to(gout + head, 8));
     for (int32_t k = 0; k < n && vec; ++k)

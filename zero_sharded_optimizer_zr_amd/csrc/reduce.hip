@@ -126,9 +126,7 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
     ContribTable<MaxN> c = {};
     for (int32_t k = 0; k < n; ++k)
         c.p[k] = static_cast<const uint16_t *>(contribs[k]);
-    int64_t head = (int64_t)(((16 - (reinterpret_cast<uintptr_t>(out) & 15)) & 15) / 2);
-    if (head > numel)
-        head = numel;
+    const int64_t head = line_head16(out, numel);
     bool vec = true;
     for (int32_t k = 0; k < n && vec; ++k)
         vec = aligned_to(c.p[k] + head, 16);

@@ -70,6 +70,32 @@ inline dim3 xcd_grid_of(int64_t tiles)
 
 inline bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
+// First element of a streaming kernel's vector body, at most 63 and never past
+// n: where the 2-byte array b16 starts a 128-byte line, so that its wave-wide
+// accesses cover whole lines.  Elements before it (and the tail after the last
+// vector group) are done element-wise.  A body starting 32 or 48 bytes into a
+// line ran the AdamW kernel at 0.67 of peak against 0.76 on whole lines.
+inline int64_t line_head16(const void *b16, int64_t n)
+{
+    const int64_t h = (int64_t)(((128 - (reinterpret_cast<uintptr_t>(b16) & 127)) & 127) / 2);
+    return h < n ? h : n;
+}
+
+// The same for a kernel led by the fp32 array f32: where f32 starts a 128-byte
+// line and, when one element index does both (the usual case of arrays sliced
+// at the same element offset from line-aligned buffers), where the 2-byte array
+// b16 does too.  Either way f32's 16-byte phase at the head is the one the
+// vector body needs.
+inline int64_t line_head32(const float *f32, const void *b16, int64_t n)
+{
+    const uintptr_t a = reinterpret_cast<uintptr_t>(f32);
+    int64_t h = (int64_t)(((128 - (a & 127)) & 127) / 4);
+    const int64_t h2 = line_head16(b16, 64);
+    if (((a + 4 * (uintptr_t)h2) & 127) == 0)
+        h = h2;
+    return h < n ? h : n;
+}
+
 inline bool overlaps(const void *a, int64_t abytes, const void *b, int64_t bbytes)
 {
     auto x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
