@@ -416,10 +416,12 @@ __global__ __launch_bounds__(kBlock) void unpack_int4_kernel(QBatch batch, int64
 
 // int4 batches of at most kFewDesc descriptors (whole shards: a flat model's
 // gather) run two chunks per lane with the tiles in XCD runs; larger batches
-// (a model's tensors) run four chunks per lane in launch order.  Measured on
-// the gathers of the 7e9 flat model over 4 ranks and of the Llama- and
-// GPT-style layouts (MI355X, same buffers): 0.790 against 0.760 for the first,
-// 0.786-0.800 against 0.683-0.685 for the others.
+// (a model's tensors) run four chunks per lane in launch order.  Measured on the
+// gathers of flat models (4 shards of 1.75e9 or 1.95e9 elements, 64 of 1.1e8)
+// and of the Llama- and GPT-style layouts (MI355X, same buffers), the rule
+// picks the faster of the two on each: 0.784 and 0.779 against 0.769 and 0.734
+// for the four-shard gathers, 0.734 against 0.673 for 64 shards, 0.796-0.802
+// against 0.673-0.682 for the model layouts.
 zr_status launch_batches(const std::vector<QDesc> &pieces, int lg_block, bool int4, hipStream_t st)
 {
     size_t i = 0;
