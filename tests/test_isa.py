@@ -24,7 +24,8 @@ CSRC = os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "csrc")
 # counts are static instructions of the kernel body; the head/tail element
 # paths use narrow accesses, which are not pinned.
 #   AdamW: dwordx4 in/out of master, m, v; dwordx2 of gradient in, copy out.
-#   reduce (8-pointer table, XCD order): two batches of 4 contribution loads.
+#   reduce (8-pointer table, XCD order): two batches of 4 contribution loads;
+#   for 7-8 contributions: 8 eight-byte loads at once, one eight-byte store.
 #   fused: master/m/v as AdamW, 8 dwordx2 contribution loads, dwordx2 copy.
 #   copy: aligned or funnel-shifted (two) loads, one store per lane.
 #   int8 quantizer: 4 chunks of 16-byte loads per tile, 8-byte code stores
@@ -37,6 +38,7 @@ KERNELS = [
     ("adamw.hip", "adamw_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                             "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
     ("reduce.hip", "reduce_vec_kernelILi8ELb1E", {"global_load_dwordx4": 8, "global_store_dwordx4": 1}),
+    ("reduce.hip", "reduce4_vec_kernelILb0E", {"global_load_dwordx2": 8, "global_store_dwordx2": 1}),
     ("fused.hip", "fused_vec_kernelILi8ELb1ELb0E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                                     "global_load_dwordx2": 8, "global_store_dwordx2": 1}),
     ("fp16.hip", "adamw_f16_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
@@ -98,5 +100,6 @@ def test_kernel_shape(asm, src, frag, counts):
         lines = [ln for ln in body if ln.split()[0] == op]
         assert len(lines) == want, f"{op}: {len(lines)} in the body, expected {want}"
         assert all(ln.rstrip().endswith(" nt") for ln in lines), f"{op} without the non-temporal hint"
-    wide = [ln for ln in body if ln.split()[0] in ("global_load_dwordx4", "global_store_dwordx4")]
-    assert wide, "no 16-byte global access"
+    wide = [ln for ln in body if ln.split()[0] in ("global_load_dwordx4", "global_store_dwordx4",
+                                                   "global_load_dwordx2", "global_store_dwordx2")]
+    assert wide, "no 8- or 16-byte global access"

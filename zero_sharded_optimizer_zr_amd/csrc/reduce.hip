@@ -16,8 +16,10 @@
 // (the cap alone gained nothing at n <= 8 in this arrangement); n = 64 at 2 per
 // CU in the default order 5.8 -> 6.1-6.3 TB/s, where the XCD order lost a
 // tenth.  Two 8-element chunks per lane (twice the loads in flight) lost 3-4%
-// at n = 4 and n = 8 at every cap from 3 to 5 workgroups per CU.  The n device
-// pointers travel by value in the kernel arguments.
+// at n = 4 and n = 8 at every cap from 3 to 5 workgroups per CU.  For 7 and 8
+// contributions a second kernel takes 4 elements per lane with all n 8-byte
+// loads in flight at once (see kFourPerLaneMinN).  The n device pointers travel
+// by value in the kernel arguments.
 //
 // Sources (web pages on DeepSpeed ZeRO-3): "From DDP to ZeRO: memory sharding"
 // blog (111qqz.com), "ZeRO-2: why gradients can be sharded too" (ReduceScatter
@@ -29,6 +31,14 @@
 namespace zr {
 
 constexpr int kLoadBatch = 4;  // contribution loads in flight per lane
+
+// From this many contributions (up to 8) the 4-elements-per-lane kernel runs:
+// 8 one-pass 8-byte loads per lane beat two batches of 4 16-byte loads.
+// Measured on MI355X (same buffers, 1.95e9 elements unless noted): n = 8
+// 0.775 of peak against 0.751 (the GPT shard's 1.2e8: 0.777 against 0.737),
+// n = 7 0.768 against 0.758, n = 6 0.731 against 0.769, n = 5 0.686 against
+// 0.776, n = 4 0.649 against 0.802.
+constexpr int32_t kFourPerLaneMinN = 7;
 
 // Dynamic LDS reserved per workgroup (160 KB per CU): residency cap by n.
 inline size_t residency_cap_lds(int32_t n)
@@ -110,6 +120,44 @@ __global__ __launch_bounds__(kBlock) void reduce_vec_kernel(ContribTable<MaxN> c
     }
 }
 
+// 7 or 8 contributions, 4 elements per lane: one 8-byte load per contribution,
+// all of them in flight before the sum (ascending k, the same bits as above),
+// one 8-byte store, at most 5 workgroups per CU; tiles in launch order (in XCD
+// runs when kXcd: 3% slower at n = 8).
+template <bool kXcd>
+__global__ __launch_bounds__(kBlock) void reduce4_vec_kernel(ContribTable<8> c, int32_t n, uint16_t *out, int64_t numel,
+                                                             int64_t head, int64_t groups, MeanDivisor d)
+{
+    u32x2 *o2 = reinterpret_cast<u32x2 *>(out + head);
+    const int64_t first = kXcd ? xcd_first_tile() : (int64_t)blockIdx.x;
+    for (int64_t i = first * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
+        u32x2 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (u < n)
+                x[u] = load_stream(reinterpret_cast<const u32x2 *>(c.p[u] + head) + i);
+        float acc[4] = {bf16_lo(x[0].x), bf16_hi(x[0].x), bf16_lo(x[0].y), bf16_hi(x[0].y)};
+#pragma unroll
+        for (int u = 1; u < 8; ++u)
+            if (u < n) {
+                acc[0] += bf16_lo(x[u].x);
+                acc[1] += bf16_hi(x[u].x);
+                acc[2] += bf16_lo(x[u].y);
+                acc[3] += bf16_hi(x[u].y);
+            }
+        store_stream(o2 + i, u32x2{pack_bf16x2(finish_mean(acc[0], d), finish_mean(acc[1], d)),
+                                   pack_bf16x2(finish_mean(acc[2], d), finish_mean(acc[3], d))});
+    }
+    if (blockIdx.x == 0) {
+        int64_t tail_start = head + 4 * groups;
+        int64_t edge = head + (numel - tail_start);  // at most 63 + 3
+        if ((int64_t)threadIdx.x < edge) {
+            int64_t j = (int64_t)threadIdx.x < head ? (int64_t)threadIdx.x : tail_start + (threadIdx.x - head);
+            out[j] = reduce_one(c, n, j, d);
+        }
+    }
+}
+
 // Fallback when the buffers' 16-byte phases disagree: element-wise, same bits.
 template <int MaxN>
 __global__ __launch_bounds__(kBlock) void reduce_scalar_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
@@ -127,6 +175,17 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
     for (int32_t k = 0; k < n; ++k)
         c.p[k] = static_cast<const uint16_t *>(contribs[k]);
     const int64_t head = line_head16(out, numel);
+    if constexpr (MaxN == 8) {
+        // 7 or 8 contributions: 4 elements per lane, every load in flight at once
+        bool vec4 = n >= kFourPerLaneMinN;
+        for (int32_t k = 0; k < n && vec4; ++k)
+            vec4 = aligned_to(c.p[k] + head, 8);
+        if (vec4) {
+            const int64_t groups = (numel - head) / 4, tiles = (groups + kBlock - 1) / kBlock;
+            return launch(reduce4_vec_kernel<false>, grid_of(tiles), dim3(kBlock), 32 * 1024, st, c, n, out, numel,
+                          head, groups, d);
+        }
+    }
     bool vec = true;
     for (int32_t k = 0; k < n && vec; ++k)
         vec = aligned_to(c.p[k] + head, 16);
