@@ -76,12 +76,14 @@ def test_reduce_f16_bit_exact(n):
         assert read_record(ls)[2] == 0
 
 
-def test_reduce_f16_extremes_subnormals_and_flag():
+@pytest.mark.parametrize("n", [3, 8])   # 8: the 4-elements-per-lane kernel
+def test_reduce_f16_extremes_subnormals_and_flag(n):
     device()
-    rng = np.random.default_rng(4)
+    rng = np.random.default_rng(4 + n)
     size = 9000
-    # magnitudes across the whole fp16 range, including subnormal means and 65504
-    vals = [rng.choice([-1, 1], size) * 2.0 ** rng.uniform(-26, 16, size) for _ in range(3)]
+    # magnitudes across the whole fp16 range (below its largest value, planted
+    # next), including subnormal means and 65504
+    vals = [rng.choice([-1, 1], size) * 2.0 ** rng.uniform(-26, 15.99, size) for _ in range(n)]
     vals[0][:8] = [65504, -65504, 65504, 2.0 ** -24, -(2.0 ** -24), 0.0, -0.0, 2.0 ** -14]
     contribs = [f16(v) for v in vals]
     ls = record()

@@ -43,6 +43,7 @@ KERNELS = [
                                                     "global_load_dwordx2": 8, "global_store_dwordx2": 1}),
     ("fp16.hip", "adamw_f16_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                                "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
+    ("fp16.hip", "reduce4_f16_vec_kernel", {"global_load_dwordx2": 8, "global_store_dwordx2": 1}),
     ("copy.hip", "copy_kernel", {"global_load_dwordx4": 2, "global_store_dwordx4": 1}),
     ("unpack_quant.hip", "unpack_int8_kernel", {"global_store_dwordx4": 9}),
     ("quant.hip", "quantize_vec_kernelILi2048ELi127E", {"global_load_dwordx4": 4, "global_store_dwordx2": 4}),

@@ -155,6 +155,49 @@ __global__ __launch_bounds__(kBlock) void reduce_f16_vec_kernel(ContribTable<Max
     }
 }
 
+// 7 or 8 contributions: 4 elements per lane with every 8-byte load in flight at
+// once, tiles in launch order, as the bf16 reduce does for the same counts.
+__global__ __launch_bounds__(kBlock) void reduce4_f16_vec_kernel(ContribTable<8> c, int32_t n, uint16_t *out,
+                                                                 int64_t numel, int64_t head, int64_t groups,
+                                                                 MeanDivisor d, zr_loss_scale *ls)
+{
+    u32x2 *o2 = reinterpret_cast<u32x2 *>(out + head);
+    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+        u32x2 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (u < n)
+                x[u] = load_stream(reinterpret_cast<const u32x2 *>(c.p[u] + head) + i);
+        float acc[4] = {f16_lo(x[0].x), f16_hi(x[0].x), f16_lo(x[0].y), f16_hi(x[0].y)};
+#pragma unroll
+        for (int u = 1; u < 8; ++u)
+            if (u < n) {
+                acc[0] += f16_lo(x[u].x);
+                acc[1] += f16_hi(x[u].x);
+                acc[2] += f16_lo(x[u].y);
+                acc[3] += f16_hi(x[u].y);
+            }
+        const u32x2 r{pack_f16x2(finish_mean(acc[0], d), finish_mean(acc[1], d)),
+                      pack_f16x2(finish_mean(acc[2], d), finish_mean(acc[3], d))};
+        store_stream(o2 + i, r);
+        if (ls)
+            flag_if_any(f16_nonfinite(r.x & 0xffffu) || f16_nonfinite(r.x >> 16) || f16_nonfinite(r.y & 0xffffu) ||
+                            f16_nonfinite(r.y >> 16),
+                        ls);
+    }
+    if (blockIdx.x == 0) {
+        int64_t tail_start = head + 4 * groups;
+        int64_t edge = head + (numel - tail_start);  // at most 63 + 3
+        if ((int64_t)threadIdx.x < edge) {
+            int64_t j = (int64_t)threadIdx.x < head ? (int64_t)threadIdx.x : tail_start + (threadIdx.x - head);
+            uint32_t h = reduce_one_f16(c, n, j, d);
+            out[j] = (uint16_t)h;
+            if (ls && f16_nonfinite(h))
+                ls->found_inf = 1;
+        }
+    }
+}
+
 template <int MaxN>
 __global__ __launch_bounds__(kBlock) void reduce_f16_scalar_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
                                                                    int64_t numel, MeanDivisor d, zr_loss_scale *ls)
@@ -281,6 +324,16 @@ static zr_status reduce_f16_launch(const void *const *contribs, int32_t n, int64
         c.p[k] = static_cast<const uint16_t *>(contribs[k]);
     const MeanDivisor d = mean_divisor(n);
     const int64_t head = line_head16(out, numel);
+    if constexpr (MaxN == 8) {
+        bool vec4 = n >= 7;  // as the bf16 reduce (kFourPerLaneMinN)
+        for (int32_t k = 0; k < n && vec4; ++k)
+            vec4 = aligned_to(c.p[k] + head, 8);
+        if (vec4) {
+            const int64_t groups = (numel - head) / 4, tiles = (groups + kBlock - 1) / kBlock;
+            return launch(reduce4_f16_vec_kernel, grid_of(tiles), dim3(kBlock), 32 * 1024, st, c, n, out, numel, head,
+                          groups, d, ls);
+        }
+    }
     bool vec = true;
     for (int32_t k = 0; k < n && vec; ++k)
         vec = aligned_to(c.p[k] + head, 16);
