@@ -26,7 +26,9 @@ CSRC = os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "csrc")
 #   AdamW: dwordx4 in/out of master, m, v; dwordx2 of gradient in, copy out.
 #   reduce (8-pointer table, XCD order): two batches of 4 contribution loads;
 #   for 7-8 contributions: 8 eight-byte loads at once, one eight-byte store.
-#   fused: master/m/v as AdamW, 8 dwordx2 contribution loads, dwordx2 copy.
+#   fused: master/m/v as AdamW, dwordx2 contribution loads (one batch of up to
+#   8 in flight; its 8 guarded loads appear twice in the compiled body), dwordx2
+#   copy.
 #   copy: aligned or funnel-shifted (two) loads, one store per lane.
 #   int8 quantizer: 4 chunks of 16-byte loads per tile, 8-byte code stores
 #   (int4: 4-byte code stores, beside the scale stores of the same width).
@@ -40,7 +42,7 @@ KERNELS = [
     ("reduce.hip", "reduce_vec_kernelILi8ELb1E", {"global_load_dwordx4": 8, "global_store_dwordx4": 1}),
     ("reduce.hip", "reduce4_vec_kernelILb0E", {"global_load_dwordx2": 8, "global_store_dwordx2": 1}),
     ("fused.hip", "fused_vec_kernelILi8ELb1ELb0E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
-                                                    "global_load_dwordx2": 8, "global_store_dwordx2": 1}),
+                                                    "global_load_dwordx2": 16, "global_store_dwordx2": 1}),
     ("fp16.hip", "adamw_f16_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                                "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
     ("fp16.hip", "reduce4_f16_vec_kernel", {"global_load_dwordx2": 8, "global_store_dwordx2": 1}),

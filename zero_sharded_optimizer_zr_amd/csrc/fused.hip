@@ -10,14 +10,15 @@
 // for bit that of zr_reduce_slice followed by zr_adamw_step.
 //
 // Each lane takes 4 consecutive elements: dwordx2 loads of the contributions
-// (four in flight at a time), dwordx4 loads and stores of master, m and v, a
-// dwordx2 store of the copy; non-temporal, one group per lane over a grid that
-// covers the shard, residency capped per contribution count with reserved LDS
-// the kernel never touches.  Tiles dealt to the XCDs in runs (as the reduce
-// does), eight elements per lane, and eight or sixteen contribution loads in
-// flight all measured slower on MI355X (same buffers: n = 4 6.12 against
-// 5.87-5.89 TB/s for the XCD order; n = 64 5.80 against 5.49-5.54 for wider
-// batches, 5.25-5.66 for eight elements per lane).
+// (all of them in flight for up to 8, else four at a time), dwordx4 loads and
+// stores of master, m and v, a dwordx2 store of the copy; non-temporal, one
+// group per lane over a grid that covers the shard, residency capped per
+// contribution count with reserved LDS the kernel never touches.  Tiles dealt
+// to the XCDs in runs (as the reduce does), eight elements per lane, and
+// eight or sixteen contribution loads in flight at n = 64 all measured slower
+// on MI355X (same buffers: n = 4 6.12 against 5.87-5.89 TB/s for the XCD
+// order; n = 64 5.80 against 5.49-5.54 for wider batches, 5.25-5.66 for eight
+// elements per lane).
 //
 // Above 24 contributions the entry point runs the reduce kernel and then the
 // AdamW kernel instead (see kFusedMaxN), with the mean in grad_out or, when only
@@ -35,7 +36,11 @@
 
 namespace zr {
 
-constexpr int kFusedBatch = 4;  // contribution loads in flight per lane
+// Contribution loads in flight per lane: all of them for up to 8 contributions
+// (at n = 8, 1.1-2.5% faster than two batches of 4 on the 1T and GPT shards),
+// batches of 4 above.
+template <int MaxN>
+constexpr int fused_batch() { return MaxN == 8 ? 8 : 4; }
 
 // Largest contribution count the one-pass kernel takes when a two-pass schedule
 // is possible.  Its saving is the bf16 mean's write and read (2 or 4 of 2n + 26
@@ -94,14 +99,15 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(ContribTable<MaxN> c,
         f32x4 mm = load_stream(m4 + i);
         f32x4 vv = load_stream(v4 + i);
         float acc[4];
-        for (int32_t k = 0; k < n; k += kFusedBatch) {
-            u32x2 x[kFusedBatch];
+        constexpr int kB = fused_batch<MaxN>();
+        for (int32_t k = 0; k < n; k += kB) {
+            u32x2 x[kB];
 #pragma unroll
-            for (int u = 0; u < kFusedBatch; ++u)
+            for (int u = 0; u < kB; ++u)
                 if (k + u < n)
                     x[u] = load_stream(reinterpret_cast<const u32x2 *>(c.p[k + u] + head) + i);
 #pragma unroll
-            for (int u = 0; u < kFusedBatch; ++u) {
+            for (int u = 0; u < kB; ++u) {
                 if (k + u == 0) {
                     acc[0] = bf16_lo(x[u].x);
                     acc[1] = bf16_hi(x[u].x);
