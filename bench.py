@@ -436,6 +436,12 @@ def fp16_leg(w, lay, b, e, S, frags, params, st, hp, t_step, args, stream):
     skipped = int(ls.cpu()[3])
     out = {"path": "pack+reduce_f16+adamw_f16+loss_scale_update+unpack", "ms_per_step": round(wall, 4),
            "value": S / (wall * 1e-3), "unit": "elements/s", "skipped_steps": skipped, "kernels": stats}
+    # The overflow check for gradients reduced by other means, timed on its own
+    # over the same finite shard (it only ever sets the flag, so the record
+    # stays clear).
+    _, chk = time_path([("check_finite_f16", lambda: zr.zr_check_finite_f16(grad, ls, stream=stream), 2 * S)],
+                       args.warmup, args.steps, stream)
+    out["beside_the_step"] = chk
     del own, contribs, grad, param, master, m, v
     torch.cuda.empty_cache()
     return out
