@@ -24,7 +24,7 @@ CSRC = os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "csrc")
 # counts are static instructions of the kernel body; the head/tail element
 # paths use narrow accesses, which are not pinned.
 #   AdamW: dwordx4 in/out of master, m, v; dwordx2 of gradient in, copy out.
-#   reduce (8-pointer table, XCD order): two batches of 4 contribution loads;
+#   reduce (8-pointer table): two batches of 4 contribution loads;
 #   for 7-8 contributions: 8 eight-byte loads at once, one eight-byte store.
 #   fused: master/m/v as AdamW, dwordx2 contribution loads (one batch of up to
 #   8 in flight; its 8 guarded loads appear twice in the compiled body), dwordx2
@@ -39,8 +39,8 @@ CSRC = os.path.join(ROOT, "zero_sharded_optimizer_zr_amd", "csrc")
 KERNELS = [
     ("adamw.hip", "adamw_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                             "global_load_dwordx2": 1, "global_store_dwordx2": 1}),
-    ("reduce.hip", "reduce_vec_kernelILi8ELb1E", {"global_load_dwordx4": 8, "global_store_dwordx4": 1}),
-    ("reduce.hip", "reduce4_vec_kernelILb0E", {"global_load_dwordx2": 8, "global_store_dwordx2": 1}),
+    ("reduce.hip", "reduce_vec_kernelILi8EE", {"global_load_dwordx4": 8, "global_store_dwordx4": 1}),
+    ("reduce.hip", "reduce4_vec_kernel", {"global_load_dwordx2": 8, "global_store_dwordx2": 1}),
     ("fused.hip", "fused_vec_kernelILi8ELb1ELb0E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
                                                     "global_load_dwordx2": 16, "global_store_dwordx2": 1}),
     ("fp16.hip", "adamw_f16_vec_kernelILb1E", {"global_load_dwordx4": 3, "global_store_dwordx4": 3,
@@ -51,8 +51,8 @@ KERNELS = [
     ("quant.hip", "quantize_vec_kernelILi2048ELi127E", {"global_load_dwordx4": 4, "global_store_dwordx2": 4}),
     ("quant.hip", "quantize_vec_kernelILi2048ELi7E", {"global_load_dwordx4": 4}),
     ("quant.hip", "dequantize_vec_kernelILi2048ELi7E", {"global_store_dwordx4": 4}),
-    ("unpack_quant.hip", "unpack_int4_kernelILi2ELb1E", {"global_store_dwordx4": 9}),
-    ("unpack_quant.hip", "unpack_int4_kernelILi4ELb0E", {"global_store_dwordx4": 25}),
+    ("unpack_quant.hip", "unpack_int4_kernelILi2ELi0E", {"global_store_dwordx4": 9}),
+    ("unpack_quant.hip", "unpack_int4_kernelILi4ELi1E", {"global_store_dwordx4": 25}),
 ]
 
 

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kBlock) void adamw_vec_kernel(const uint16_t *grad,
     f32x4 *v4 = reinterpret_cast<f32x4 *>(v + head);
     u32x2 *p2 = kParam ? reinterpret_cast<u32x2 *>(param + head) : nullptr;
 
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kAdamwOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         u32x2 g = load_stream(g2 + i);
         f32x4 a = load_stream(th4 + i);
         f32x4 mm = load_stream(m4 + i);
@@ -111,14 +111,15 @@ int adamw_scalar_slots(ScalarSlot *out)
 zr_status adamw_run(const uint16_t *g, float *master, float *exp_avg, float *exp_avg_sq, uint16_t *p, int64_t numel,
                     const AdamWScalars &s, hipStream_t st)
 {
-    // elements before master reaches a 16-byte boundary; the other buffers must
-    // then be aligned too (16 B for fp32, 8 B for bf16) for the vector body
+    // elements before master starts a 128-byte line (the gradient's line too
+    // when one index starts both); the other buffers must then be aligned
+    // (16 B for fp32, 8 B for bf16) for the vector body
     const int64_t head = line_head32(master, g, numel);
     bool vec = aligned_to(exp_avg + head, 16) && aligned_to(exp_avg_sq + head, 16) && aligned_to(g + head, 8) &&
                (!p || aligned_to(p + head, 8));
     if (vec) {
         int64_t groups = (numel - head) / 4;
-        dim3 grid = grid_of((groups + kBlock - 1) / kBlock);
+        dim3 grid = order_grid<kAdamwOrder>((groups + kBlock - 1) / kBlock);
         if (p)
             return launch(adamw_vec_kernel<true>, grid, dim3(kBlock), ZR_ADAMW_LDS_CAP, st, g, master, exp_avg,
                           exp_avg_sq, p, numel, head, groups, s);

@@ -132,11 +132,11 @@ __device__ __forceinline__ void copy_tile(const CopyBatch &batch, int64_t tile)
     }
 }
 
-// Tiles in XCD runs (the grid is a multiple of kXcds); a workgroup takes tile
-// xcd_first_tile(), then every gridDim.x-th after it.
+// Tiles in the order kCopyOrder; a workgroup takes tile first_tile(), then
+// every gridDim.x-th after it.
 __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch, int64_t total_tiles)
 {
-    for (int64_t tile = xcd_first_tile(); tile < total_tiles; tile += gridDim.x)
+    for (int64_t tile = first_tile<kCopyOrder>(); tile < total_tiles; tile += gridDim.x)
         copy_tile(batch, tile);
 }
 
@@ -169,7 +169,7 @@ zr_status launch_pieces(const std::vector<Piece> &pieces, hipStream_t st)
             ++i;
         }
         batch.count = count;
-        zr_status s = launch(copy_kernel, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
+        zr_status s = launch(copy_kernel, order_grid<kCopyOrder>(tiles), dim3(kBlock), 0, st, batch, tiles);
         if (s != ZR_OK)
             return s;
     }

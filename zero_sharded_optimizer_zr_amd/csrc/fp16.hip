@@ -93,16 +93,15 @@ __device__ __forceinline__ uint32_t reduce_one_f16(const ContribTable<MaxN> &c, 
     return f32_to_f16(finish_mean(sum, d));
 }
 
-// Tiles of kBlock groups, in XCD runs when kXcd (grid a multiple of 8), as the
-// bf16 reduce.
-template <int MaxN, bool kXcd>
+// Tiles of kBlock groups in the bf16 reduce's order.
+template <int MaxN>
 __global__ __launch_bounds__(kBlock) void reduce_f16_vec_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
                                                                 int64_t numel, int64_t head, int64_t groups,
                                                                 MeanDivisor d, zr_loss_scale *ls)
 {
     u32x4 *o4 = reinterpret_cast<u32x4 *>(out + head);
-    const int64_t first = kXcd ? xcd_first_tile() : (int64_t)blockIdx.x;
-    for (int64_t i = first * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
+    constexpr int kOrder = MaxN <= 8 ? kReduceOrder : kReduceWideOrder;
+    for (int64_t i = first_tile<kOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         float acc[8];
         for (int32_t k = 0; k < n; k += 4) {
             u32x4 x[4];
@@ -162,7 +161,7 @@ __global__ __launch_bounds__(kBlock) void reduce4_f16_vec_kernel(ContribTable<8>
                                                                  MeanDivisor d, zr_loss_scale *ls)
 {
     u32x2 *o2 = reinterpret_cast<u32x2 *>(out + head);
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kReduce4Order>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         u32x2 x[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -216,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void check_finite_kernel(const uint16_t *gr
                                                               int64_t groups, zr_loss_scale *ls)
 {
     const u32x4 *g4 = reinterpret_cast<const u32x4 *>(grad + head);
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kCheckFiniteOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         u32x4 x = load_stream(g4 + i);
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
         bool bad = false;
@@ -268,7 +267,7 @@ __global__ __launch_bounds__(kBlock) void adamw_f16_vec_kernel(const uint16_t *g
     int32_t skip = ls->found_inf;
     float scale = ls->scale;
 
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kAdamwOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         u32x2 g = load_stream(g2 + i);
         f32x4 a = load_stream(th4 + i);
         f32x4 mm = load_stream(m4 + i);
@@ -330,8 +329,8 @@ static zr_status reduce_f16_launch(const void *const *contribs, int32_t n, int64
             vec4 = aligned_to(c.p[k] + head, 8);
         if (vec4) {
             const int64_t groups = (numel - head) / 4, tiles = (groups + kBlock - 1) / kBlock;
-            return launch(reduce4_f16_vec_kernel, grid_of(tiles), dim3(kBlock), 32 * 1024, st, c, n, out, numel, head,
-                          groups, d, ls);
+            return launch(reduce4_f16_vec_kernel, order_grid<kReduce4Order>(tiles), dim3(kBlock), 32 * 1024, st, c,
+                          n, out, numel, head, groups, d, ls);
         }
     }
     bool vec = true;
@@ -343,12 +342,8 @@ static zr_status reduce_f16_launch(const void *const *contribs, int32_t n, int64
     // residency cap and tile order as the bf16 reduce
     const int64_t groups = (numel - head) / 8, tiles = (groups + kBlock - 1) / kBlock;
     const size_t lds = n > 8 ? 80 * 1024 : (n > 4 ? 40 * 1024 : 32 * 1024);
-    if constexpr (MaxN <= 8)
-        return launch(reduce_f16_vec_kernel<MaxN, true>, xcd_grid_of(tiles), dim3(kBlock), lds, st, c, n, out, numel,
-                      head, groups, d, ls);
-    else
-        return launch(reduce_f16_vec_kernel<MaxN, false>, grid_of(tiles), dim3(kBlock), lds, st, c, n, out, numel,
-                      head, groups, d, ls);
+    return launch(reduce_f16_vec_kernel<MaxN>, order_grid<MaxN <= 8 ? kReduceOrder : kReduceWideOrder>(tiles),
+                  dim3(kBlock), lds, st, c, n, out, numel, head, groups, d, ls);
 }
 
 inline zr_status check_ls(const char *who, const void *ls)
@@ -458,7 +453,7 @@ extern "C" zr_status zr_check_finite_f16(const void *grad, int64_t numel, zr_los
     auto g = static_cast<const uint16_t *>(grad);
     const int64_t head = line_head16(g, numel);
     const int64_t groups = (numel - head) / 8;
-    return launch(check_finite_kernel, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock), 0,
+    return launch(check_finite_kernel, order_grid<kCheckFiniteOrder>((groups + kBlock - 1) / kBlock), dim3(kBlock), 0,
                   static_cast<hipStream_t>(stream), g, numel, head, groups, ls);
 }
 
@@ -501,7 +496,7 @@ extern "C" zr_status zr_adamw_step_f16(const void *grad, float *master, float *e
         return launch(adamw_f16_scalar_kernel, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, g,
                       master, exp_avg, exp_avg_sq, p, numel, s, ls);
     const int64_t groups = (numel - head) / 4;
-    dim3 grid = grid_of((groups + kBlock - 1) / kBlock);
+    dim3 grid = order_grid<kAdamwOrder>((groups + kBlock - 1) / kBlock);
     if (p)
         return launch(adamw_f16_vec_kernel<true>, grid, dim3(kBlock), kAdamwF16Lds, st, g, master, exp_avg,
                       exp_avg_sq, p, numel, head, groups, s, ls);

@@ -94,7 +94,8 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(ContribTable<MaxN> c,
     u32x2 *p2 = kParam ? reinterpret_cast<u32x2 *>(param + head) : nullptr;
     u32x2 *o2 = kGrad ? reinterpret_cast<u32x2 *>(gout + head) : nullptr;
 
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    constexpr int kOrder = MaxN <= 8 ? kFusedOrder : kFusedWideOrder;
+    for (int64_t i = first_tile<kOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         f32x4 a = load_stream(th4 + i);
         f32x4 mm = load_stream(m4 + i);
         f32x4 vv = load_stream(v4 + i);
@@ -167,8 +168,9 @@ static zr_status fused_vec_launch(const ContribTable<MaxN> &c, int32_t n, float 
                                   uint16_t *param, uint16_t *gout, int64_t numel, int64_t head, int64_t groups,
                                   const MeanDivisor &d, const AdamWScalars &s, hipStream_t st)
 {
-    return launch(fused_vec_kernel<MaxN, kParam, kGrad>, grid_of((groups + kBlock - 1) / kBlock), dim3(kBlock),
-                  fused_cap_lds(n), st, c, n, master, m, v, param, gout, numel, head, groups, d, s);
+    return launch(fused_vec_kernel<MaxN, kParam, kGrad>,
+                  order_grid<MaxN <= 8 ? kFusedOrder : kFusedWideOrder>((groups + kBlock - 1) / kBlock),
+                  dim3(kBlock), fused_cap_lds(n), st, c, n, master, m, v, param, gout, numel, head, groups, d, s);
 }
 
 template <int MaxN>

@@ -266,11 +266,11 @@ template <int B, int kQ>
 __global__ __launch_bounds__(kBlock) void quantize_vec_kernel(const uint16_t *src, int64_t numel, uint8_t *q,
                                                               float *scales, int64_t ntiles)
 {
-    // workgroups in XCD runs (grid a multiple of 8), kBlock / 64 tiles each,
-    // then the same again gridDim.x workgroups further on
+    // workgroups in the order kQuantizeOrder, kBlock / 64 tiles each, then the
+    // same again gridDim.x workgroups further on
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
-    for (int64_t tile = xcd_first_tile() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t tile = first_tile<kQuantizeOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
          tile < ntiles; tile += stride) {
         const int64_t base = tile * kTile;
         if (base + kTile <= numel)
@@ -357,7 +357,9 @@ __global__ __launch_bounds__(kBlock) void dequantize_vec_kernel(const uint8_t *q
                                                                 uint16_t *dst, int64_t ntiles)
 {
     const int lane = threadIdx.x & 63;
-    for (int64_t tile = wave_id(); tile < ntiles; tile += (int64_t)gridDim.x * (kBlock / 64)) {
+    constexpr int kOrder = kQ == 127 ? kDequantize8Order : kDequantize4Order;
+    for (int64_t tile = first_tile<kOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         tile < ntiles; tile += (int64_t)gridDim.x * (kBlock / 64)) {
         const int64_t base = tile * kTile;
         if (base + kTile <= numel)
             dequantize_tile<B, true, kQ>(q, scales, numel, dst, base, lane);
@@ -408,7 +410,7 @@ zr_status quantize_launch(const char *who, const void *src, int64_t numel, int32
         return launch(quantize_scalar_kernel<kQ>, grid_of((nblocks + 3) / 4), dim3(kBlock), 0, st, s, numel, block,
                       q, scales, nblocks);
     const int64_t ntiles = (numel + kTile - 1) / kTile;
-    const dim3 grid = xcd_grid_of((ntiles + 3) / 4);
+    const dim3 grid = order_grid<kQuantizeOrder>((ntiles + 3) / 4);
     constexpr size_t lds = 32 * 1024;  // 5 workgroups per CU
     switch (block) {
     case 256: return launch(quantize_vec_kernel<256, kQ>, grid, dim3(kBlock), lds, st, s, numel, q, scales, ntiles);
@@ -448,7 +450,7 @@ zr_status dequantize_launch(const char *who, const uint8_t *q, const float *scal
         return launch(dequantize_scalar_kernel<kQ>, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, q,
                       scales, numel, block, d);
     const int64_t ntiles = (numel + kTile - 1) / kTile;
-    const dim3 grid = grid_of((ntiles + 3) / 4);
+    const dim3 grid = order_grid<kQ == 127 ? kDequantize8Order : kDequantize4Order>((ntiles + 3) / 4);
     switch (block) {
     case 256: return launch(dequantize_vec_kernel<256, kQ>, grid, dim3(kBlock), 0, st, q, scales, numel, d, ntiles);
     case 512: return launch(dequantize_vec_kernel<512, kQ>, grid, dim3(kBlock), 0, st, q, scales, numel, d, ntiles);

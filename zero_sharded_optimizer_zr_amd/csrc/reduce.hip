@@ -75,19 +75,25 @@ __device__ __forceinline__ void set8(float (&acc)[8], u32x4 x)
     acc[7] = bf16_hi(x.w);
 }
 
+// Tile order of the 8-element reduce: up to 8 contributions, or more.
+template <int MaxN>
+constexpr int reduce_order()
+{
+    return MaxN <= 8 ? kReduceOrder : kReduceWideOrder;
+}
+
 // Vector body over `groups` groups of 8 elements from element `head` (where
 // every contribution and the output are 16-byte aligned), in tiles of kBlock
-// groups (in XCD runs when kXcd, from a grid that is a multiple of 8); block 0
-// also does the unaligned head [0, head) and the tail element-wise.  out may
-// be c.p[0]: each lane reads all its inputs before it writes.
-template <int MaxN, bool kXcd>
+// groups in the order reduce_order<MaxN>(); block 0 also does the unaligned
+// head [0, head) and the tail element-wise.  out may be c.p[0]: each lane
+// reads all its inputs before it writes.
+template <int MaxN>
 __global__ __launch_bounds__(kBlock) void reduce_vec_kernel(ContribTable<MaxN> c, int32_t n, uint16_t *out,
                                                             int64_t numel, int64_t head, int64_t groups,
                                                             MeanDivisor d)
 {
     u32x4 *o4 = reinterpret_cast<u32x4 *>(out + head);
-    const int64_t first = kXcd ? xcd_first_tile() : (int64_t)blockIdx.x;
-    for (int64_t i = first * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<reduce_order<MaxN>()>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         float acc[8];
         for (int32_t k = 0; k < n; k += kLoadBatch) {
             u32x4 x[kLoadBatch];
@@ -122,15 +128,13 @@ __global__ __launch_bounds__(kBlock) void reduce_vec_kernel(ContribTable<MaxN> c
 
 // 7 or 8 contributions, 4 elements per lane: one 8-byte load per contribution,
 // all of them in flight before the sum (ascending k, the same bits as above),
-// one 8-byte store, at most 5 workgroups per CU; tiles in launch order (in XCD
-// runs when kXcd: 3% slower at n = 8).
-template <bool kXcd>
+// one 8-byte store, at most 5 workgroups per CU; tiles in the order
+// kReduce4Order.
 __global__ __launch_bounds__(kBlock) void reduce4_vec_kernel(ContribTable<8> c, int32_t n, uint16_t *out, int64_t numel,
                                                              int64_t head, int64_t groups, MeanDivisor d)
 {
     u32x2 *o2 = reinterpret_cast<u32x2 *>(out + head);
-    const int64_t first = kXcd ? xcd_first_tile() : (int64_t)blockIdx.x;
-    for (int64_t i = first * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kReduce4Order>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         u32x2 x[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -182,8 +186,8 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
             vec4 = aligned_to(c.p[k] + head, 8);
         if (vec4) {
             const int64_t groups = (numel - head) / 4, tiles = (groups + kBlock - 1) / kBlock;
-            return launch(reduce4_vec_kernel<false>, grid_of(tiles), dim3(kBlock), 32 * 1024, st, c, n, out, numel,
-                          head, groups, d);
+            return launch(reduce4_vec_kernel, order_grid<kReduce4Order>(tiles), dim3(kBlock), 32 * 1024, st, c, n,
+                          out, numel, head, groups, d);
         }
     }
     bool vec = true;
@@ -191,12 +195,8 @@ static zr_status reduce_launch(const void *const *contribs, int32_t n, int64_t n
         vec = aligned_to(c.p[k] + head, 16);
     if (vec) {
         const int64_t groups = (numel - head) / 8, tiles = (groups + kBlock - 1) / kBlock;
-        if constexpr (MaxN <= 8)  // tiles in XCD runs for up to 8 contributions
-            return launch(reduce_vec_kernel<MaxN, true>, xcd_grid_of(tiles), dim3(kBlock), residency_cap_lds(n), st,
-                          c, n, out, numel, head, groups, d);
-        else
-            return launch(reduce_vec_kernel<MaxN, false>, grid_of(tiles), dim3(kBlock), residency_cap_lds(n), st, c,
-                          n, out, numel, head, groups, d);
+        return launch(reduce_vec_kernel<MaxN>, order_grid<reduce_order<MaxN>()>(tiles), dim3(kBlock),
+                      residency_cap_lds(n), st, c, n, out, numel, head, groups, d);
     }
     return launch(reduce_scalar_kernel<MaxN>, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, c, n,
                   out, numel, d);

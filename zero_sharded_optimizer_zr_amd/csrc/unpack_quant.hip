@@ -398,19 +398,19 @@ __device__ __forceinline__ void unpack_int8_tile(const QBatch &batch, int64_t ti
     }
 }
 
-// int8: tiles in XCD runs (the grid is a multiple of kXcds); a workgroup takes
-// tile xcd_first_tile(), then every gridDim.x-th after it.
+// int8: tiles in the order kUnpack8Order; a workgroup takes tile
+// first_tile(), then every gridDim.x-th after it.
 __global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64_t total_tiles)
 {
-    for (int64_t tile = xcd_first_tile(); tile < total_tiles; tile += gridDim.x)
+    for (int64_t tile = first_tile<kUnpack8Order>(); tile < total_tiles; tile += gridDim.x)
         unpack_int8_tile(batch, tile);
 }
 
-// int4: PL chunks per lane; tiles in XCD runs (kXcdOrder) or in launch order.
-template <int PL, bool kXcdOrder>
+// int4: PL chunks per lane, tiles in the order kOrder.
+template <int PL, int kOrder>
 __global__ __launch_bounds__(kBlock) void unpack_int4_kernel(QBatch batch, int64_t total_tiles)
 {
-    for (int64_t tile = kXcdOrder ? xcd_first_tile() : (int64_t)blockIdx.x; tile < total_tiles; tile += gridDim.x)
+    for (int64_t tile = first_tile<kOrder>(); tile < total_tiles; tile += gridDim.x)
         unpack_int4_tile<PL>(batch, tile);
 }
 
@@ -443,11 +443,13 @@ zr_status launch_batches(const std::vector<QDesc> &pieces, int lg_block, bool in
         i += count;
         zr_status s;
         if (!int4)
-            s = launch(unpack_int8_kernel, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
+            s = launch(unpack_int8_kernel, order_grid<kUnpack8Order>(tiles), dim3(kBlock), 0, st, batch, tiles);
         else if (few)
-            s = launch(unpack_int4_kernel<kPerLane4Few, true>, xcd_grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
+            s = launch(unpack_int4_kernel<kPerLane4Few, kUnpack4FewOrder>, order_grid<kUnpack4FewOrder>(tiles),
+                       dim3(kBlock), 0, st, batch, tiles);
         else
-            s = launch(unpack_int4_kernel<kPerLane4Many, false>, grid_of(tiles), dim3(kBlock), 0, st, batch, tiles);
+            s = launch(unpack_int4_kernel<kPerLane4Many, kUnpack4ManyOrder>, order_grid<kUnpack4ManyOrder>(tiles),
+                       dim3(kBlock), 0, st, batch, tiles);
         if (s != ZR_OK)
             return s;
     }

@@ -70,15 +70,54 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 __device__ __forceinline__ int64_t global_tid() { return (int64_t)blockIdx.x * kBlock + threadIdx.x; }
 __device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * kBlock; }
 
-// MI355X deals workgroups round-robin to its 8 XCDs (workgroup b runs on XCD
-// b mod 8), each with its own L2.  With a grid that is a multiple of kXcds,
-// tile (b mod 8) * (grid / 8) + b / 8 gives every XCD one contiguous run of
-// tiles instead of every eighth one; the next tile of a workgroup that loops
-// is gridDim.x further on.
+// Tile orders.  MI355X deals workgroups round-robin to its 8 XCDs (workgroup b
+// runs on XCD b mod 8), each with its own L2.  A launch of G workgroups takes
+// its tiles in rounds of G (a workgroup that loops takes the tile gridDim.x
+// further on), and first_tile<R>() orders the tiles of a round:
+//  - R = 1: launch order, workgroup b takes tile b;
+//  - R > 1: runs of R consecutive tiles per XCD: in every group of 8R tiles,
+//    XCD x takes tiles xR ... xR + R - 1, one after another; the round's last,
+//    partial group stays in launch order;
+//  - R = kOneRun: one run per XCD, grid / 8 tiles long (grid a multiple of 8).
+// Each is a permutation of the round's tiles, so any grid covers the data.
 constexpr int kXcds = 8;
-__device__ __forceinline__ int64_t xcd_first_tile()
+constexpr int kOneRun = 0;
+#ifdef ZR_ORDER_ALL
+#define ZR_ORDER(r) ZR_ORDER_ALL
+#else
+#define ZR_ORDER(r) (r)
+#endif
+template <int R>
+__device__ __forceinline__ int64_t first_tile()
 {
-    return (int64_t)(blockIdx.x % kXcds) * (gridDim.x / kXcds) + blockIdx.x / kXcds;
+    const int64_t b = blockIdx.x;
+    if constexpr (R == kOneRun) {
+        return (b % kXcds) * (gridDim.x / kXcds) + b / kXcds;
+    } else if constexpr (R == 1) {
+        return b;
+    } else {
+        constexpr int64_t group = (int64_t)kXcds * R;
+        if (b >= (int64_t)gridDim.x / group * group)
+            return b;
+        const int64_t j = b / kXcds;
+        return (j / R) * group + (b % kXcds) * R + j % R;
+    }
 }
+
+// Tile order of each streaming kernel family.
+constexpr int kAdamwOrder = ZR_ORDER(256);  // AdamW (bf16 and fp16) and its access-pattern kernel
+constexpr int kFusedOrder = ZR_ORDER(kOneRun);  // reduce + AdamW in one pass, up to 8 contributions
+constexpr int kFusedWideOrder = ZR_ORDER(256);  // the same, 9 to 24
+constexpr int kReduceOrder = ZR_ORDER(256);  // means of up to 6 contributions (bf16 and fp16)
+constexpr int kReduce4Order = ZR_ORDER(256);  // means of 7 or 8
+constexpr int kReduceWideOrder = ZR_ORDER(1);  // means of more than 8
+constexpr int kCopyOrder = ZR_ORDER(kOneRun);  // pack / unpack
+constexpr int kQuantizeOrder = ZR_ORDER(64);  // workgroups of 4 tiles (8192 elements)
+constexpr int kDequantize8Order = ZR_ORDER(64);
+constexpr int kDequantize4Order = ZR_ORDER(1);
+constexpr int kUnpack8Order = ZR_ORDER(kOneRun);
+constexpr int kUnpack4FewOrder = ZR_ORDER(kOneRun);  // a batch of at most 8 descriptors
+constexpr int kUnpack4ManyOrder = ZR_ORDER(1);
+constexpr int kCheckFiniteOrder = ZR_ORDER(256);
 
 }  // namespace zr

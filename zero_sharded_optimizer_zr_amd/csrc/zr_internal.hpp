@@ -68,6 +68,14 @@ inline dim3 xcd_grid_of(int64_t tiles)
     return dim3((unsigned)tiles);
 }
 
+// Grid for `tiles` tiles taken in the order first_tile<R>() gives (R = 0, one
+// run per XCD, needs a multiple of 8).
+template <int R>
+inline dim3 order_grid(int64_t tiles)
+{
+    return R == 0 ? xcd_grid_of(tiles) : grid_of(tiles);
+}
+
 inline bool aligned_to(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // First element of a streaming kernel's vector body, at most 63 and never past

@@ -25,7 +25,7 @@ using namespace zr;
 __global__ __launch_bounds__(kBlock) void adamw_pattern_kernel(const u32x2 *grad, f32x4 *master, f32x4 *m, f32x4 *v,
                                                                 u32x2 *param, int64_t groups, float one)
 {
-    for (int64_t i = global_tid(); i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kAdamwOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         u32x2 g = load_stream(grad + i);
         f32x4 a = load_stream(master + i);
         f32x4 mm = load_stream(m + i);
@@ -53,8 +53,10 @@ extern "C" __attribute__((visibility("default"))) int zr_measure_adamw_pattern(c
         return -1;
     const int64_t groups = numel / 4;
     int64_t blocks = (groups + kBlock - 1) / kBlock;
-    if (blocks > 0x7fffffff)
-        blocks = 0x7fffffff;
+    if (kAdamwOrder == kOneRun)
+        blocks = (blocks + kXcds - 1) / kXcds * kXcds;
+    if (blocks > 0x7ffffff8)
+        blocks = 0x7ffffff8;
     hipLaunchKernelGGL(adamw_pattern_kernel, dim3((unsigned)blocks), dim3(kBlock), 32 * 1024,
                        static_cast<hipStream_t>(stream), static_cast<const u32x2 *>(grad),
                        reinterpret_cast<f32x4 *>(master), reinterpret_cast<f32x4 *>(m),
