@@ -4,8 +4,8 @@ consecutive tiles go to the 8 XCDs R at a time (XCD x takes tiles xR ...
 xR + R - 1 of each group); the round's last, partial group is in launch order.
 The sizes here span several full groups and a ragged partial one for each
 kernel that uses such runs (AdamW, the means of up to 8 contributions, the
-fused reduce + AdamW above 8 contributions, the fp16 mean, finite check and
-AdamW, the quantizers and the int8 dequantizer), so every part of the order
+fused reduce + AdamW, the fp16 mean, finite check and AdamW, the quantizers
+and the int8 dequantizer), so every part of the order
 runs: each output must equal the oracle's bit for bit, and stay the same with
 the grid capped at one full group plus a few workgroups (rounds that mix both
 parts, and rounds of launch order only), with nothing written outside the

@@ -83,6 +83,14 @@ __global__ void loss_scale_update_kernel(zr_loss_scale *ls, int32_t window, floa
 
 // ------------------------------------------------------- gradient mean ------
 
+// Tile orders (first_tile) of the mean, as the bf16 reduce: runs of 256 tiles
+// per XCD up to 8 contributions, launch order above; the finite check in runs
+// of 256 too (6-8% over launch order on the same buffers).
+constexpr int kReduceOrder = ZR_ORDER(256);
+constexpr int kReduce4Order = ZR_ORDER(256);
+constexpr int kReduceWideOrder = ZR_ORDER(1);
+constexpr int kCheckFiniteOrder = ZR_ORDER(256);
+
 template <int MaxN>
 __device__ __forceinline__ uint32_t reduce_one_f16(const ContribTable<MaxN> &c, int32_t n, int64_t j,
                                                    const MeanDivisor &d)

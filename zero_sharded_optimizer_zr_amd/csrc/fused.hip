@@ -82,6 +82,10 @@ __device__ __forceinline__ void fused_one(const ContribTable<MaxN> &c, int32_t n
 // Vector body over `groups` groups of 4 elements from element `head` (master,
 // m, v 16-byte aligned there; contributions, copy and mean 8-byte aligned);
 // block 0 also does the head [0, head) and the tail element-wise.
+// Tile order (first_tile): runs of 256 tiles per XCD, 1-8% faster than launch
+// order on the same buffers (most on shards of about 1e8 elements).
+constexpr int kFusedOrder = ZR_ORDER(256);
+
 template <int MaxN, bool kParam, bool kGrad>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(ContribTable<MaxN> c, int32_t n, float *master, float *m,
                                                            float *v, uint16_t *param, uint16_t *gout, int64_t numel,
@@ -94,8 +98,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(ContribTable<MaxN> c,
     u32x2 *p2 = kParam ? reinterpret_cast<u32x2 *>(param + head) : nullptr;
     u32x2 *o2 = kGrad ? reinterpret_cast<u32x2 *>(gout + head) : nullptr;
 
-    constexpr int kOrder = MaxN <= 8 ? kFusedOrder : kFusedWideOrder;
-    for (int64_t i = first_tile<kOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kFusedOrder>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
         f32x4 a = load_stream(th4 + i);
         f32x4 mm = load_stream(m4 + i);
         f32x4 vv = load_stream(v4 + i);
@@ -168,8 +171,7 @@ static zr_status fused_vec_launch(const ContribTable<MaxN> &c, int32_t n, float 
                                   uint16_t *param, uint16_t *gout, int64_t numel, int64_t head, int64_t groups,
                                   const MeanDivisor &d, const AdamWScalars &s, hipStream_t st)
 {
-    return launch(fused_vec_kernel<MaxN, kParam, kGrad>,
-                  order_grid<MaxN <= 8 ? kFusedOrder : kFusedWideOrder>((groups + kBlock - 1) / kBlock),
+    return launch(fused_vec_kernel<MaxN, kParam, kGrad>, order_grid<kFusedOrder>((groups + kBlock - 1) / kBlock),
                   dim3(kBlock), fused_cap_lds(n), st, c, n, master, m, v, param, gout, numel, head, groups, d, s);
 }
 

@@ -75,6 +75,14 @@ __device__ __forceinline__ void set8(float (&acc)[8], u32x4 x)
     acc[7] = bf16_hi(x.w);
 }
 
+// Tile orders (first_tile): runs of 256 tiles per XCD for up to 8
+// contributions (1 MB of each contribution per run; +0.5-3.5% over the single
+// run per XCD or launch order, on the same buffers), launch order above 8
+// (runs lost up to 4% at n = 64).
+constexpr int kReduceOrder = ZR_ORDER(256);  // 8 elements per lane, up to 6 contributions
+constexpr int kReduce4Order = ZR_ORDER(256);  // 4 per lane, 7 or 8
+constexpr int kReduceWideOrder = ZR_ORDER(1);  // more than 8
+
 // Tile order of the 8-element reduce: up to 8 contributions, or more.
 template <int MaxN>
 constexpr int reduce_order()

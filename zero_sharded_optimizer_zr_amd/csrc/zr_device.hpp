@@ -104,20 +104,10 @@ __device__ __forceinline__ int64_t first_tile()
     }
 }
 
-// Tile order of each streaming kernel family.
-constexpr int kAdamwOrder = ZR_ORDER(256);  // AdamW (bf16 and fp16) and its access-pattern kernel
-constexpr int kFusedOrder = ZR_ORDER(kOneRun);  // reduce + AdamW in one pass, up to 8 contributions
-constexpr int kFusedWideOrder = ZR_ORDER(256);  // the same, 9 to 24
-constexpr int kReduceOrder = ZR_ORDER(256);  // means of up to 6 contributions (bf16 and fp16)
-constexpr int kReduce4Order = ZR_ORDER(256);  // means of 7 or 8
-constexpr int kReduceWideOrder = ZR_ORDER(1);  // means of more than 8
-constexpr int kCopyOrder = ZR_ORDER(kOneRun);  // pack / unpack
-constexpr int kQuantizeOrder = ZR_ORDER(64);  // workgroups of 4 tiles (8192 elements)
-constexpr int kDequantize8Order = ZR_ORDER(64);
-constexpr int kDequantize4Order = ZR_ORDER(1);
-constexpr int kUnpack8Order = ZR_ORDER(kOneRun);
-constexpr int kUnpack4FewOrder = ZR_ORDER(kOneRun);  // a batch of at most 8 descriptors
-constexpr int kUnpack4ManyOrder = ZR_ORDER(1);
-constexpr int kCheckFiniteOrder = ZR_ORDER(256);
+// Tile order of the AdamW kernels (bf16 and fp16 gradients) and of their
+// access-pattern kernel: runs of 256 tiles (1 MB of each fp32 array) per XCD,
+// 2.6-2.9% faster than launch order on the same buffers.  The other kernel
+// families set theirs beside their kernels.
+constexpr int kAdamwOrder = ZR_ORDER(256);
 
 }  // namespace zr
