@@ -1,7 +1,8 @@
 """The streaming kernels take their tiles in runs per XCD: a launch of G
 workgroups works in rounds of G tiles, and within a round, groups of 8R
 consecutive tiles go to the 8 XCDs R at a time (XCD x takes tiles xR ...
-xR + R - 1 of each group); the round's last, partial group is in launch order.
+xR + R - 1 of each group, or for the means of up to 8 contributions the slot
+rotated by the group's index); the round's last, partial group is in launch order.
 The sizes here span several full groups and a ragged partial one for each
 kernel that uses such runs (AdamW, the means of up to 8 contributions, the
 fused reduce + AdamW, the fp16 mean, finite check and AdamW, the quantizers

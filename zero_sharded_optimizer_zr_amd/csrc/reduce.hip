@@ -77,11 +77,12 @@ __device__ __forceinline__ void set8(float (&acc)[8], u32x4 x)
 
 // Tile orders (first_tile): runs of 256 tiles per XCD for up to 8
 // contributions (1 MB of each contribution per run; +0.5-3.5% over the single
-// run per XCD or launch order, on the same buffers), launch order above 8
-// (runs lost up to 4% at n = 64).
+// run per XCD or launch order, on the same buffers), rotated from group to
+// group (another 2%); launch order above 8 (runs lost up to 4% at n = 64).
 constexpr int kReduceOrder = ZR_ORDER(256);  // 8 elements per lane, up to 6 contributions
 constexpr int kReduce4Order = ZR_ORDER(256);  // 4 per lane, 7 or 8
 constexpr int kReduceWideOrder = ZR_ORDER(1);  // more than 8
+constexpr bool kReduceRotate = true;
 
 // Tile order of the 8-element reduce: up to 8 contributions, or more.
 template <int MaxN>
@@ -101,7 +102,8 @@ __global__ __launch_bounds__(kBlock) void reduce_vec_kernel(ContribTable<MaxN> c
                                                             MeanDivisor d)
 {
     u32x4 *o4 = reinterpret_cast<u32x4 *>(out + head);
-    for (int64_t i = first_tile<reduce_order<MaxN>()>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<reduce_order<MaxN>(), kReduceRotate>() * kBlock + threadIdx.x; i < groups;
+         i += grid_stride()) {
         float acc[8];
         for (int32_t k = 0; k < n; k += kLoadBatch) {
             u32x4 x[kLoadBatch];
@@ -142,7 +144,8 @@ __global__ __launch_bounds__(kBlock) void reduce4_vec_kernel(ContribTable<8> c, 
                                                              int64_t head, int64_t groups, MeanDivisor d)
 {
     u32x2 *o2 = reinterpret_cast<u32x2 *>(out + head);
-    for (int64_t i = first_tile<kReduce4Order>() * kBlock + threadIdx.x; i < groups; i += grid_stride()) {
+    for (int64_t i = first_tile<kReduce4Order, kReduceRotate>() * kBlock + threadIdx.x; i < groups;
+         i += grid_stride()) {
         u32x2 x[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)

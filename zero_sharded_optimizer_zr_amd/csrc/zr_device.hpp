@@ -75,9 +75,11 @@ __device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * k
 // its tiles in rounds of G (a workgroup that loops takes the tile gridDim.x
 // further on), and first_tile<R>() orders the tiles of a round:
 //  - R = 1: launch order, workgroup b takes tile b;
-//  - R > 1: runs of R consecutive tiles per XCD: in every group of 8R tiles,
-//    XCD x takes tiles xR ... xR + R - 1, one after another; the round's last,
-//    partial group stays in launch order;
+//  - R > 1: runs of R consecutive tiles per XCD: in group g of 8R tiles, XCD x
+//    takes the R tiles of slot x (tiles xR ... xR + R - 1 of the group), or with
+//    kRotate those of slot (x + g) mod 8, so that its runs move through the
+//    slots from group to group; the round's last, partial group stays in
+//    launch order;
 //  - R = kOneRun: one run per XCD, grid / 8 tiles long (grid a multiple of 8).
 // Each is a permutation of the round's tiles, so any grid covers the data.
 constexpr int kXcds = 8;
@@ -87,7 +89,7 @@ constexpr int kOneRun = 0;
 #else
 #define ZR_ORDER(r) (r)
 #endif
-template <int R>
+template <int R, bool kRotate = false>
 __device__ __forceinline__ int64_t first_tile()
 {
     const int64_t b = blockIdx.x;
@@ -99,14 +101,16 @@ __device__ __forceinline__ int64_t first_tile()
         constexpr int64_t group = (int64_t)kXcds * R;
         if (b >= (int64_t)gridDim.x / group * group)
             return b;
-        const int64_t j = b / kXcds;
-        return (j / R) * group + (b % kXcds) * R + j % R;
+        const int64_t j = b / kXcds, g = j / R;
+        const int64_t slot = kRotate ? (b % kXcds + g) % kXcds : b % kXcds;
+        return g * group + slot * R + j % R;
     }
 }
 
 // Tile order of the AdamW kernels (bf16 and fp16 gradients) and of their
 // access-pattern kernel: runs of 256 tiles (1 MB of each fp32 array) per XCD,
-// 2.6-2.9% faster than launch order on the same buffers.  The other kernel
+// 2.6-2.9% faster than launch order on the same buffers (rotating the runs
+// moved it by -0.4 to +0.6%, so they are not rotated).  The other kernel
 // families set theirs beside their kernels.
 constexpr int kAdamwOrder = ZR_ORDER(256);
 
