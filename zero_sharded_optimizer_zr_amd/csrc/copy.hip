@@ -135,7 +135,7 @@ __device__ __forceinline__ void copy_tile(const CopyBatch &batch, int64_t tile)
 // Tiles in one contiguous run per XCD (runs of 256 tiles measured within 1%
 // of it); a workgroup takes tile first_tile(), then every gridDim.x-th after
 // it.
-constexpr int kCopyOrder = ZR_ORDER(kOneRun);
+constexpr int kCopyOrder = kOneRun;
 __global__ __launch_bounds__(kBlock) void copy_kernel(CopyBatch batch, int64_t total_tiles)
 {
     for (int64_t tile = first_tile<kCopyOrder>(); tile < total_tiles; tile += gridDim.x)

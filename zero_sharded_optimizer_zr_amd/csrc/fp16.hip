@@ -87,11 +87,11 @@ __global__ void loss_scale_update_kernel(zr_loss_scale *ls, int32_t window, floa
 // per XCD, rotated from group to group, up to 8 contributions, launch order
 // above; the finite check in runs of 256, not rotated (6-8% over launch order
 // on the same buffers; the rotation lost 1%).
-constexpr int kReduceOrder = ZR_ORDER(256);
-constexpr int kReduce4Order = ZR_ORDER(256);
-constexpr int kReduceWideOrder = ZR_ORDER(1);
+constexpr int kReduceOrder = 256;
+constexpr int kReduce4Order = 256;
+constexpr int kReduceWideOrder = 1;
 constexpr bool kReduceRotate = true;
-constexpr int kCheckFiniteOrder = ZR_ORDER(256);
+constexpr int kCheckFiniteOrder = 256;
 
 template <int MaxN>
 __device__ __forceinline__ uint32_t reduce_one_f16(const ContribTable<MaxN> &c, int32_t n, int64_t j,

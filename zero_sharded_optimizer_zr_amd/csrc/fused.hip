@@ -84,7 +84,7 @@ __device__ __forceinline__ void fused_one(const ContribTable<MaxN> &c, int32_t n
 // block 0 also does the head [0, head) and the tail element-wise.
 // Tile order (first_tile): runs of 256 tiles per XCD, 1-8% faster than launch
 // order on the same buffers (most on shards of about 1e8 elements).
-constexpr int kFusedOrder = ZR_ORDER(256);
+constexpr int kFusedOrder = 256;
 
 template <int MaxN, bool kParam, bool kGrad>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(ContribTable<MaxN> c, int32_t n, float *master, float *m,

@@ -265,9 +265,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t *src, int64_t numel
 // elements): runs of 64 per XCD for the quantizers (1.6-5.8% over one run per
 // XCD) and the int8 dequantizer (about 5% over launch order); launch order for
 // the int4 dequantizer (runs lost 2-6%).
-constexpr int kQuantizeOrder = ZR_ORDER(64);
-constexpr int kDequantize8Order = ZR_ORDER(64);
-constexpr int kDequantize4Order = ZR_ORDER(1);
+constexpr int kQuantizeOrder = 64;
+constexpr int kDequantize8Order = 64;
+constexpr int kDequantize4Order = 1;
 
 // Vector path: src 16-byte aligned, codes 8-byte (int8) or 4-byte (int4) aligned.
 template <int B, int kQ>

@@ -79,9 +79,9 @@ __device__ __forceinline__ void set8(float (&acc)[8], u32x4 x)
 // contributions (1 MB of each contribution per run; +0.5-3.5% over the single
 // run per XCD or launch order, on the same buffers), rotated from group to
 // group (another 2%); launch order above 8 (runs lost up to 4% at n = 64).
-constexpr int kReduceOrder = ZR_ORDER(256);  // 8 elements per lane, up to 6 contributions
-constexpr int kReduce4Order = ZR_ORDER(256);  // 4 per lane, 7 or 8
-constexpr int kReduceWideOrder = ZR_ORDER(1);  // more than 8
+constexpr int kReduceOrder = 256;  // 8 elements per lane, up to 6 contributions
+constexpr int kReduce4Order = 256;  // 4 per lane, 7 or 8
+constexpr int kReduceWideOrder = 1;  // more than 8
 constexpr bool kReduceRotate = true;
 
 // Tile order of the 8-element reduce: up to 8 contributions, or more.

@@ -401,9 +401,9 @@ __device__ __forceinline__ void unpack_int8_tile(const QBatch &batch, int64_t ti
 // Tile orders (first_tile): one contiguous run per XCD for the int8 kernel and
 // for int4 batches of a few descriptors, launch order for int4 batches of many
 // (runs lost 2-9% there).
-constexpr int kUnpack8Order = ZR_ORDER(kOneRun);
-constexpr int kUnpack4FewOrder = ZR_ORDER(kOneRun);
-constexpr int kUnpack4ManyOrder = ZR_ORDER(1);
+constexpr int kUnpack8Order = kOneRun;
+constexpr int kUnpack4FewOrder = kOneRun;
+constexpr int kUnpack4ManyOrder = 1;
 
 // int8: a workgroup takes tile first_tile(), then every gridDim.x-th after it.
 __global__ __launch_bounds__(kBlock) void unpack_int8_kernel(QBatch batch, int64_t total_tiles)

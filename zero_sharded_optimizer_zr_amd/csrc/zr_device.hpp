@@ -84,11 +84,6 @@ __device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * k
 // Each is a permutation of the round's tiles, so any grid covers the data.
 constexpr int kXcds = 8;
 constexpr int kOneRun = 0;
-#ifdef ZR_ORDER_ALL
-#define ZR_ORDER(r) ZR_ORDER_ALL
-#else
-#define ZR_ORDER(r) (r)
-#endif
 template <int R, bool kRotate = false>
 __device__ __forceinline__ int64_t first_tile()
 {
@@ -112,6 +107,6 @@ __device__ __forceinline__ int64_t first_tile()
 // 2.6-2.9% faster than launch order on the same buffers (rotating the runs
 // moved it by -0.4 to +0.6%, so they are not rotated).  The other kernel
 // families set theirs beside their kernels.
-constexpr int kAdamwOrder = ZR_ORDER(256);
+constexpr int kAdamwOrder = 256;
 
 }  // namespace zr
