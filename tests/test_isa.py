@@ -106,3 +106,13 @@ def test_kernel_shape(asm, src, frag, counts):
     wide = [ln for ln in body if ln.split()[0] in ("global_load_dwordx4", "global_store_dwordx4",
                                                    "global_load_dwordx2", "global_store_dwordx2")]
     assert wide, "no 8- or 16-byte global access"
+
+
+def test_int4_dequantize_issues_its_loads_first(asm):
+    """The int4 dequantizer's whole-tile path issues the code loads of all 4
+    chunks of a lane before its first store (codes and output may alias for
+    the compiler, so a load after a store would wait for it)."""
+    body, _ = kernel_body(asm["quant.hip"], "dequantize_vec_kernelILi2048ELi7E")
+    ops = [ln.split()[0] for ln in body]
+    first_store = ops.index("global_store_dwordx4")
+    assert ops[:first_store].count("global_load_dword") >= 4, ops[:first_store]

@@ -263,11 +263,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t *src, int64_t numel
 
 // Tile orders (first_tile), in workgroups of kBlock / 64 tiles (8192
 // elements): runs of 64 per XCD for the quantizers (1.6-5.8% over one run per
-// XCD) and the int8 dequantizer (about 5% over launch order); launch order for
-// the int4 dequantizer (runs lost 2-6%).
+// XCD) and the dequantizers (int8 about 5% over launch order, int4 4%).
 constexpr int kQuantizeOrder = 64;
-constexpr int kDequantize8Order = 64;
-constexpr int kDequantize4Order = 1;
+constexpr int kDequantizeOrder = 64;
 
 // Vector path: src 16-byte aligned, codes 8-byte (int8) or 4-byte (int4) aligned.
 template <int B, int kQ>
@@ -319,42 +317,68 @@ __global__ __launch_bounds__(kBlock) void quantize_scalar_kernel(const uint16_t 
     }
 }
 
-template <int B, bool kFull, int kQ>
-__device__ __forceinline__ void dequantize_tile(const uint8_t *q, const float *scales, int64_t numel, uint16_t *dst,
-                                                int64_t base, int lane)
+// A whole tile.  int4: every code and scale load of the lane's chunks is
+// issued before the first store.  The codes and the output may alias as far as
+// the compiler knows, so a load placed after a store waits for it; chunk by
+// chunk, each wave waited out one memory latency per chunk, and issuing the
+// loads first made the kernel 7.5% faster (12% with runs of 64 workgroups per
+// XCD; same buffers, same bits).  int8 stays chunk by chunk: its loads first
+// measured 2.3% slower.
+template <int B, int kQ>
+__device__ __forceinline__ void dequantize_full_tile(const uint8_t *q, const float *scales, uint16_t *dst,
+                                                     int64_t base, int lane)
 {
+    if constexpr (kQ == 127) {
 #pragma unroll
-    for (int c = 0; c < kTileChunks; ++c) {
-        if (!kFull && base + c * kChunk >= numel)
-            break;
-        const int64_t i = base + c * kChunk + lane * kLaneVec;
-        // B >= 512: one block per chunk, the same for every lane (a scalar load)
-        const float s = B >= kChunk ? scales[(base + c * kChunk) / B] : (kFull || i < numel ? scales[i / B] : 0.0f);
-        if (kFull) {
+        for (int c = 0; c < kTileChunks; ++c) {
+            const int64_t i = base + c * kChunk + lane * kLaneVec;
+            // B >= 512: one block per chunk, the same for every lane
+            const float s = B >= kChunk ? scales[(base + c * kChunk) / B] : scales[i / B];
+            const u32x2 w = load_stream(reinterpret_cast<const u32x2 *>(q + i));
             u32x4 o;
-            if constexpr (kQ == 127) {
-                u32x2 w = load_stream(reinterpret_cast<const u32x2 *>(q + i));
 #pragma unroll
-                for (int h = 0; h < 4; ++h) {
-                    const uint32_t word = w[h / 2] >> (16 * (h % 2));
-                    o[h] = pack_bf16x2((float)(int8_t)word * s, (float)(int8_t)(word >> 8) * s);
-                }
-            } else {
-                const uint32_t w = load_stream(reinterpret_cast<const uint32_t *>(q + i / 2));
-#pragma unroll
-                for (int h = 0; h < 4; ++h)
-                    o[h] = pack_bf16x2((float)nibble_code(w, 2 * h) * s, (float)nibble_code(w, 2 * h + 1) * s);
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t word = w[h / 2] >> (16 * (h % 2));
+                o[h] = pack_bf16x2((float)(int8_t)word * s, (float)(int8_t)(word >> 8) * s);
             }
             store_stream(reinterpret_cast<u32x4 *>(dst + i), o);
-        } else {
+        }
+    } else {
+        uint32_t w[kTileChunks];
+        float s[kTileChunks];
 #pragma unroll
-            for (int e = 0; e < kLaneVec; ++e) {
-                if (i + e >= numel)
-                    break;
-                const int32_t code = kQ == 127 ? (int32_t)(int8_t)q[i + e]
-                                               : nibble_code(q[(i + e) / 2], (int)((i + e) & 1));
-                dst[i + e] = (uint16_t)f32_to_bf16((float)code * s);
-            }
+        for (int c = 0; c < kTileChunks; ++c) {
+            const int64_t i = base + c * kChunk + lane * kLaneVec;
+            w[c] = load_stream(reinterpret_cast<const uint32_t *>(q + i / 2));
+            s[c] = B >= kChunk ? scales[(base + c * kChunk) / B] : scales[i / B];
+        }
+#pragma unroll
+        for (int c = 0; c < kTileChunks; ++c) {
+            const int64_t i = base + c * kChunk + lane * kLaneVec;
+            u32x4 o;
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+                o[h] = pack_bf16x2((float)nibble_code(w[c], 2 * h) * s[c], (float)nibble_code(w[c], 2 * h + 1) * s[c]);
+            store_stream(reinterpret_cast<u32x4 *>(dst + i), o);
+        }
+    }
+}
+
+// The last tile, which may end inside a chunk: element by element.
+template <int B, int kQ>
+__device__ __forceinline__ void dequantize_last_tile(const uint8_t *q, const float *scales, int64_t numel,
+                                                     uint16_t *dst, int64_t base, int lane)
+{
+    for (int c = 0; c < kTileChunks; ++c) {
+        if (base + c * kChunk >= numel)
+            break;
+        const int64_t i = base + c * kChunk + lane * kLaneVec;
+#pragma unroll
+        for (int e = 0; e < kLaneVec; ++e) {
+            if (i + e >= numel)
+                break;
+            const int32_t code = kQ == 127 ? (int32_t)(int8_t)q[i + e] : nibble_code(q[(i + e) / 2], (int)((i + e) & 1));
+            dst[i + e] = (uint16_t)f32_to_bf16((float)code * scales[(i + e) / B]);
         }
     }
 }
@@ -365,14 +389,13 @@ __global__ __launch_bounds__(kBlock) void dequantize_vec_kernel(const uint8_t *q
                                                                 uint16_t *dst, int64_t ntiles)
 {
     const int lane = threadIdx.x & 63;
-    constexpr int kOrder = kQ == 127 ? kDequantize8Order : kDequantize4Order;
-    for (int64_t tile = first_tile<kOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t tile = first_tile<kDequantizeOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
          tile < ntiles; tile += (int64_t)gridDim.x * (kBlock / 64)) {
         const int64_t base = tile * kTile;
         if (base + kTile <= numel)
-            dequantize_tile<B, true, kQ>(q, scales, numel, dst, base, lane);
+            dequantize_full_tile<B, kQ>(q, scales, dst, base, lane);
         else
-            dequantize_tile<B, false, kQ>(q, scales, numel, dst, base, lane);
+            dequantize_last_tile<B, kQ>(q, scales, numel, dst, base, lane);
     }
 }
 
@@ -458,7 +481,7 @@ zr_status dequantize_launch(const char *who, const uint8_t *q, const float *scal
         return launch(dequantize_scalar_kernel<kQ>, grid_of((numel + kBlock - 1) / kBlock), dim3(kBlock), 0, st, q,
                       scales, numel, block, d);
     const int64_t ntiles = (numel + kTile - 1) / kTile;
-    const dim3 grid = order_grid<kQ == 127 ? kDequantize8Order : kDequantize4Order>((ntiles + 3) / 4);
+    const dim3 grid = order_grid<kDequantizeOrder>((ntiles + 3) / 4);
     switch (block) {
     case 256: return launch(dequantize_vec_kernel<256, kQ>, grid, dim3(kBlock), 0, st, q, scales, numel, d, ntiles);
     case 512: return launch(dequantize_vec_kernel<512, kQ>, grid, dim3(kBlock), 0, st, q, scales, numel, d, ntiles);
