@@ -313,7 +313,8 @@ def main():
                      "frac_of_copy_ceiling": round(achieved / copy_gbps, 4),
                      "pattern_ceiling": {
                          "kernel": "zr_measure_adamw_pattern: the AdamW kernel's 4 loads and 4 stores per lane, "
-                                   "launch shape and 5-per-CU cap, without its arithmetic, on the same buffers",
+                                   "launch shape, tile order and 5-per-CU cap, without its arithmetic, on the same "
+                                   "buffers",
                          "ms_avg": round(pattern_ms, 4),
                          "GBps": round(bytes_per["adamw"] / (pattern_ms * 1e-3) / 1e9, 1),
                          "frac": round(bytes_per["adamw"] / (pattern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),

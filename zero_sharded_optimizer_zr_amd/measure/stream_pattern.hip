@@ -2,8 +2,9 @@
 // pattern of the fused AdamW kernel (zr_adamw_step) with its arithmetic taken
 // out.  Same launch shape as that kernel -- 256 lanes per workgroup, 4
 // consecutive elements per lane, one group per lane over a grid that covers the
-// array, non-temporal loads and stores, 32 KB of dynamic LDS reserved and never
-// touched so that at most 5 workgroups share a CU -- and the same eight streams:
+// array, the tiles in the same order (kAdamwOrder), non-temporal loads and
+// stores, 32 KB of dynamic LDS reserved and never touched so that at most 5
+// workgroups share a CU -- and the same eight streams:
 // a dwordx2 load of the bf16 gradient, dwordx4 loads and stores of the fp32
 // master, m and v, a dwordx2 store of the bf16 copy.  Each state value is
 // multiplied by `one` (1.0 at run time, so the values stay as they were and
