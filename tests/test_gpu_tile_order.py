@@ -2,15 +2,14 @@
 workgroups works in rounds of G tiles, and within a round, groups of 8R
 consecutive tiles go to the 8 XCDs R at a time (XCD x takes tiles xR ...
 xR + R - 1 of each group, or for the means of up to 8 contributions the slot
-rotated by the group's index); the round's last, partial group is in launch order.
-The sizes here span several full groups and a ragged partial one for each
-kernel that uses such runs (AdamW, the means of up to 8 contributions, the
-fused reduce + AdamW, the fp16 mean, finite check and AdamW, the quantizers
-and the int8 dequantizer), so every part of the order
-runs: each output must equal the oracle's bit for bit, and stay the same with
-the grid capped at one full group plus a few workgroups (rounds that mix both
-parts, and rounds of launch order only), with nothing written outside the
-buffers."""
+rotated by the group's index); the round's last, partial group is in launch
+order.  The sizes here span several full groups and a ragged partial one for
+each kernel that uses such runs (AdamW, the means of up to 8 contributions,
+the fused reduce + AdamW, the fp16 mean, finite check and AdamW, the
+quantizers and dequantizers), so every part of the order runs: each output
+must equal the oracle's bit for bit, and stay the same with the grid capped at
+one full group plus a few workgroups (rounds that mix both parts, and rounds
+of launch order only), with nothing written outside the buffers."""
 import numpy as np
 import pytest
 import torch
