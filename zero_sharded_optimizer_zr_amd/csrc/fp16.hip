@@ -165,7 +165,8 @@ __global__ __launch_bounds__(kBlock) void reduce_f16_vec_kernel(ContribTable<Max
 }
 
 // 7 or 8 contributions: 4 elements per lane with every 8-byte load in flight at
-// once, tiles in launch order, as the bf16 reduce does for the same counts.
+// once, tiles in rotated runs of 256, as the bf16 reduce does for the same
+// counts.
 __global__ __launch_bounds__(kBlock) void reduce4_f16_vec_kernel(ContribTable<8> c, int32_t n, uint16_t *out,
                                                                  int64_t numel, int64_t head, int64_t groups,
                                                                  MeanDivisor d, zr_loss_scale *ls)

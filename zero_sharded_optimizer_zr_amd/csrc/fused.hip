@@ -13,12 +13,11 @@
 // (all of them in flight for up to 8, else four at a time), dwordx4 loads and
 // stores of master, m and v, a dwordx2 store of the copy; non-temporal, one
 // group per lane over a grid that covers the shard, residency capped per
-// contribution count with reserved LDS the kernel never touches.  Tiles dealt
-// to the XCDs in runs (as the reduce does), eight elements per lane, and
-// eight or sixteen contribution loads in flight at n = 64 all measured slower
-// on MI355X (same buffers: n = 4 6.12 against 5.87-5.89 TB/s for the XCD
-// order; n = 64 5.80 against 5.49-5.54 for wider batches, 5.25-5.66 for eight
-// elements per lane).
+// contribution count with reserved LDS the kernel never touches, tiles in runs
+// of 256 per XCD (kFusedOrder).  Eight elements per lane and eight or sixteen
+// contribution loads in flight at n = 64 measured slower on MI355X (same
+// buffers: n = 64 5.80 against 5.49-5.54 TB/s for wider batches, 5.25-5.66 for
+// eight elements per lane).
 //
 // Above 24 contributions the entry point runs the reduce kernel and then the
 // AdamW kernel instead (see kFusedMaxN), with the mean in grad_out or, when only

@@ -22,13 +22,12 @@
 // runs in lanes 0 .. 2048 / B - 1, which also store the tile's scales in one
 // instruction.  Bound by HBM: 3 (int8) or 2.5 (int4) bytes per element plus 4
 // per block.  The
-// quantizer's workgroups take their tiles in XCD runs, at most 5 per CU (LDS
-// reserved and never touched): on MI355X, same buffers, 1.75e9 elements,
-// B = 2048, 6.17 -> 6.53 TB/s against the default order uncapped (the XCD order
-// alone 6.31, the cap alone 6.31; 3 per CU 5.64).  The dequantizer keeps the
-// default order: there each XCD's L2 fetches the 128-byte lines of scales its
-// tiles need, 1.4% (int8) or 2.7% (int4) above the algorithmic reads, but the
-// XCD order, which removes that, ran 2% and 9-15% slower.
+// quantizer's workgroups take their tiles in runs per XCD, at most 5 per CU
+// (LDS reserved and never touched): on MI355X, same buffers, 1.75e9 elements,
+// B = 2048, one contiguous run per XCD with the cap 6.17 -> 6.53 TB/s against
+// launch order uncapped (the run alone 6.31, the cap alone 6.31; 3 per CU
+// 5.64), and runs of 64 workgroups another 1.6-5.8%.  The dequantizers take
+// runs of 64 too, uncapped (see kDequantizeOrder).
 //
 // Source (web pages on DeepSpeed ZeRO-3): ZeRO-1/2/3 concept page
 // (compassingai.com), ZeRO++ section -- qwZ quantizes the weights carried by

@@ -10,12 +10,12 @@
 // flight per lane.  With n + 1 concurrent streams the DRAM rows thrash when
 // every CU is full of waves, so the kernel caps its residency with LDS it
 // reserves and never touches, and for up to 8 contributions it deals its tiles
-// to the XCDs in contiguous runs.  Measured on MI355X against uncapped, default
-// order, on the same buffers: n = 4 at 5 workgroups per CU with the XCD order
-// 6.06 -> 6.43 TB/s; n = 8 at 4 per CU with the XCD order 5.66 -> 5.99 TB/s
-// (the cap alone gained nothing at n <= 8 in this arrangement); n = 64 at 2 per
-// CU in the default order 5.8 -> 6.1-6.3 TB/s, where the XCD order lost a
-// tenth.  Two 8-element chunks per lane (twice the loads in flight) lost 3-4%
+// to the XCDs in runs (kReduceOrder).  Measured on MI355X against uncapped,
+// launch order, on the same buffers: n = 4 at 5 workgroups per CU with one
+// contiguous run per XCD 6.06 -> 6.43 TB/s; n = 8 at 4 per CU 5.66 -> 5.99
+// TB/s (the cap alone gained nothing at n <= 8 in this arrangement), and runs
+// of 256 tiles, rotated, gained another 2-3%; n = 64 at 2 per CU in launch
+// order 5.8 -> 6.1-6.3 TB/s, where the contiguous runs lost a tenth.  Two 8-element chunks per lane (twice the loads in flight) lost 3-4%
 // at n = 4 and n = 8 at every cap from 3 to 5 workgroups per CU.  For 7 and 8
 // contributions a second kernel takes 4 elements per lane with all n 8-byte
 // loads in flight at once (see kFourPerLaneMinN).  The n device pointers travel
