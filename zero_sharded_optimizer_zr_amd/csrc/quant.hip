@@ -275,8 +275,9 @@ __global__ __launch_bounds__(kBlock) void quantize_vec_kernel(const uint16_t *sr
     // same again gridDim.x workgroups further on
     const int lane = threadIdx.x & 63;
     const int64_t stride = (int64_t)gridDim.x * (kBlock / 64);
-    for (int64_t tile = first_tile<kQuantizeOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-         tile < ntiles; tile += stride) {
+    const int64_t first =
+        first_tile<kQuantizeOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t tile = first; tile < ntiles; tile += stride) {
         const int64_t base = tile * kTile;
         if (base + kTile <= numel)
             quantize_tile<B, true, kQ>(src, numel, q, scales, base, lane);
@@ -376,7 +377,8 @@ __device__ __forceinline__ void dequantize_last_tile(const uint8_t *q, const flo
         for (int e = 0; e < kLaneVec; ++e) {
             if (i + e >= numel)
                 break;
-            const int32_t code = kQ == 127 ? (int32_t)(int8_t)q[i + e] : nibble_code(q[(i + e) / 2], (int)((i + e) & 1));
+            const int32_t code =
+                kQ == 127 ? (int32_t)(int8_t)q[i + e] : nibble_code(q[(i + e) / 2], (int)((i + e) & 1));
             dst[i + e] = (uint16_t)f32_to_bf16((float)code * scales[(i + e) / B]);
         }
     }
@@ -388,8 +390,9 @@ __global__ __launch_bounds__(kBlock) void dequantize_vec_kernel(const uint8_t *q
                                                                 uint16_t *dst, int64_t ntiles)
 {
     const int lane = threadIdx.x & 63;
-    for (int64_t tile = first_tile<kDequantizeOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-         tile < ntiles; tile += (int64_t)gridDim.x * (kBlock / 64)) {
+    const int64_t first =
+        first_tile<kDequantizeOrder>() * (kBlock / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    for (int64_t tile = first; tile < ntiles; tile += (int64_t)gridDim.x * (kBlock / 64)) {
         const int64_t base = tile * kTile;
         if (base + kTile <= numel)
             dequantize_full_tile<B, kQ>(q, scales, dst, base, lane);

@@ -15,8 +15,9 @@
 // contiguous run per XCD 6.06 -> 6.43 TB/s; n = 8 at 4 per CU 5.66 -> 5.99
 // TB/s (the cap alone gained nothing at n <= 8 in this arrangement), and runs
 // of 256 tiles, rotated, gained another 2-3%; n = 64 at 2 per CU in launch
-// order 5.8 -> 6.1-6.3 TB/s, where the contiguous runs lost a tenth.  Two 8-element chunks per lane (twice the loads in flight) lost 3-4%
-// at n = 4 and n = 8 at every cap from 3 to 5 workgroups per CU.  For 7 and 8
+// order 5.8 -> 6.1-6.3 TB/s, where the contiguous runs lost a tenth.  Two
+// 8-element chunks per lane (twice the loads in flight) lost 3-4% at n = 4
+// and n = 8 at every cap from 3 to 5 workgroups per CU.  For 7 and 8
 // contributions a second kernel takes 4 elements per lane with all n 8-byte
 // loads in flight at once (see kFourPerLaneMinN).  The n device pointers travel
 // by value in the kernel arguments.
