@@ -332,3 +332,42 @@ def test_int4_full_shard_and_gather_7b_over_4_ranks_sampled():
         assert_bits_equal(out[b0:b1].cpu().numpy().view(np.uint16), ref[0], f"window at {b0}")
     del qd, sd, out
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_dequantize_past_2_31_elements_sampled(bits):
+    """The flat dequantizers over 2^31 + 4099 elements (random codes, random
+    scales, block 2048, a ragged last tile): sampled blocks, among them those
+    around element 2^31 and the last, recomputed by the oracle."""
+    dev = device()
+    n, block = 2 ** 31 + 4099, 2048
+    nb = -(-n // block)
+    say("dequantize past 2^31, int", bits, "n", n)
+    g = torch.Generator(device=dev)
+    g.manual_seed(90 + bits)
+    if bits == 8:
+        q = torch.randint(-127, 128, (n,), dtype=torch.int8, device=dev, generator=g)
+    else:
+        q = torch.randint(0, 256, ((n + 1) // 2,), dtype=torch.uint8, device=dev, generator=g)
+        q = torch.where((q & 0xf) == 8, q ^ 0x1, q)              # no -8 codes
+        q = torch.where((q >> 4) == 8, q ^ 0x10, q)
+    sc = torch.rand(nb, dtype=torch.float32, device=dev, generator=g) * 1e-3
+    out = torch.empty(n, dtype=torch.int16, device=dev)
+    if bits == 8:
+        zr.zr_dequantize_int8(q, sc, out, block=block)
+    else:
+        zr.zr_dequantize_int4(q, sc, out, block=block)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(91)
+    edge = 2 ** 31 // block
+    picks = np.unique(np.concatenate([rng.integers(0, nb, 200), [0, edge - 1, edge, edge + 1, nb - 2, nb - 1]]))
+    sh = sc.cpu().numpy()
+    for b in picks:
+        lo, hi = int(b) * block, min(n, (int(b) + 1) * block)
+        if bits == 8:
+            ref = oracle.dequantize_int8(q[lo:hi].cpu().numpy(), sh[b:b + 1].copy(), block)
+        else:
+            ref = oracle.dequantize_int4(q[lo // 2:(hi + 1) // 2].cpu().numpy(), sh[b:b + 1].copy(), hi - lo, block)
+        assert_bits_equal(out[lo:hi].cpu().numpy().view(np.uint16), ref, f"int{bits} block {b}")
+    del q, sc, out
+    torch.cuda.empty_cache()
